@@ -1,0 +1,86 @@
+// Device-side building blocks shared by the gfx950 kernels: bf16 packing,
+// the 16x16x32 bf16 matrix-core step, wavefront reductions and fast exp2.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kascade {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16;
+
+constexpr int kWave = 64;
+
+// Finite stand-in for -infinity in running maxima: exp2(x - kNegBig) stays
+// well defined when every key seen so far is masked.
+constexpr float kNegBig = -1.0e30f;
+
+__device__ __forceinline__ float bf16_bits_to_float(u16 b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ u16 float_to_bf16_bits(float f) {
+  __bf16 h = static_cast<__bf16>(f);
+  return __builtin_bit_cast(u16, h);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// One v_mfma_f32_16x16x32_bf16: C[16x16] += A[16x32] * B[32x16].
+// Lane l supplies row (l % 16) of A and column (l % 16) of B, each as 8
+// contraction elements of lane group l / 16; the same (group, slot) pairs
+// index the contraction in A and in B. Lane l receives C rows
+// 4*(l/16) .. 4*(l/16)+3 of column l % 16.
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 load_bf16x8(const u16* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+  bf16x8 z;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) z[i] = static_cast<__bf16>(0.0f);
+  return z;
+}
+
+__device__ __forceinline__ bf16x8 pack_bf16x8(f32x4 lo, f32x4 hi) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r[i] = static_cast<__bf16>(lo[i]);
+    r[i + 4] = static_cast<__bf16>(hi[i]);
+  }
+  return r;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Reductions across the four lane groups (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float group4_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  return fmaxf(v, __shfl_xor(v, 32));
+}
+
+__device__ __forceinline__ float group4_sum(float v) {
+  v += __shfl_xor(v, 16);
+  return v + __shfl_xor(v, 32);
+}
+
+}  // namespace kascade

@@ -1,0 +1,292 @@
+// C ABI of the library (declared in include/kascade.h): argument validation,
+// workspace layout and the kernel sequence of each call. Validation is pure
+// host code and runs before anything is enqueued.
+#include <math.h>
+#include <string.h>
+
+#include "kascade.h"
+#include "kernels.hpp"
+
+namespace {
+
+using namespace kascade;
+
+constexpr size_t kAlign = 256;
+constexpr int kTargetWaves = 2048;  // about eight wavefronts per compute unit
+constexpr int kMaxGroup = 16;       // query heads per KV head handled together
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool is_decode(int op) { return op == KASCADE_OP_ANCHOR_DECODE || op == KASCADE_OP_REUSE_DECODE; }
+
+int validate(const kascade_problem* p, int op) {
+  if (!p) return KASCADE_ERR_INVALID;
+  if (op < KASCADE_OP_ANCHOR_DECODE || op > KASCADE_OP_REUSE_PREFILL) return KASCADE_ERR_INVALID;
+  if (p->batch < 1 || p->num_q_heads < 1 || p->num_kv_heads < 1 || p->head_dim < 1 ||
+      p->q_len < 1 || p->kv_len < 1 || p->top_k < 1)
+    return KASCADE_ERR_INVALID;
+  if (p->num_q_heads % p->num_kv_heads != 0) return KASCADE_ERR_INVALID;
+  if (p->dtype != KASCADE_F32 && p->dtype != KASCADE_BF16) return KASCADE_ERR_INVALID;
+  if (!(p->scale <= 0.0f) && !(p->scale > 0.0f)) return KASCADE_ERR_INVALID;  // NaN
+  // Index arithmetic inside the kernels uses 32-bit row numbers.
+  if ((long long)p->batch * p->num_q_heads * p->q_len >= (1ll << 31) ||
+      (long long)p->batch * p->num_kv_heads * p->kv_len >= (1ll << 31))
+    return KASCADE_ERR_UNSUPPORTED;
+  if (p->head_dim != 64 && p->head_dim != 128) return KASCADE_ERR_UNSUPPORTED;
+  if (p->num_q_heads / p->num_kv_heads > kMaxGroup) return KASCADE_ERR_UNSUPPORTED;
+  if (is_decode(op)) {
+    if (p->q_len != 1) return KASCADE_ERR_INVALID;
+    if (p->top_k > p->kv_len) return KASCADE_ERR_INVALID;
+  } else {
+    if (p->q_len != p->kv_len) return KASCADE_ERR_INVALID;
+    if (p->q_tile < 1) return KASCADE_ERR_INVALID;
+    if (p->q_tile != 128) return KASCADE_ERR_UNSUPPORTED;
+    if (p->dtype != KASCADE_BF16) return KASCADE_ERR_UNSUPPORTED;
+  }
+  return KASCADE_OK;
+}
+
+struct DecodeSplit {
+  int splits, keys_per_split;
+};
+
+// Spread a list of `len` keys per (b, KV head) over enough wavefronts to fill
+// the chip; each wavefront gets a multiple of 64 keys.
+DecodeSplit decode_split(const kascade_problem* p, int len) {
+  const int units = p->batch * p->num_kv_heads;
+  const int max_splits = (len + 63) / 64;
+  int splits = (kTargetWaves + units - 1) / units;
+  if (splits > max_splits) splits = max_splits;
+  if (splits < 1) splits = 1;
+  int kps = (len + splits - 1) / splits;
+  kps = (kps + 63) / 64 * 64;
+  return {(len + kps - 1) / kps, kps};
+}
+
+struct DecodeWorkspace {
+  DecodeSplit split;
+  size_t part_ml, part_o, logits, pooled, total;  // byte offsets
+};
+
+DecodeWorkspace decode_workspace(const kascade_problem* p, int op) {
+  DecodeWorkspace w{};
+  const bool anchor = op == KASCADE_OP_ANCHOR_DECODE;
+  w.split = decode_split(p, anchor ? p->kv_len : p->top_k);
+  const size_t rows = (size_t)p->batch * p->num_q_heads;
+  size_t off = 0;
+  w.part_ml = off;
+  off += align_up(rows * w.split.splits * 2 * sizeof(float));
+  w.part_o = off;
+  off += align_up(rows * w.split.splits * p->head_dim * sizeof(float));
+  if (anchor) {
+    w.logits = off;
+    off += align_up(rows * decode_logits_ld(p->kv_len) * sizeof(float));
+    w.pooled = off;
+    off += align_up((size_t)p->batch * p->num_kv_heads * p->kv_len * sizeof(float));
+  }
+  w.total = off;
+  return w;
+}
+
+struct PrefillWorkspace {
+  size_t lse2, pooled, total;
+};
+
+PrefillWorkspace prefill_workspace(const kascade_problem* p, int op) {
+  PrefillWorkspace w{};
+  if (op == KASCADE_OP_ANCHOR_PREFILL) {
+    size_t off = 0;
+    w.lse2 = off;
+    off += align_up((size_t)p->batch * p->num_q_heads * p->kv_len * sizeof(float));
+    w.pooled = off;
+    off += align_up((size_t)p->batch * p->num_kv_heads * prefill_ragged_len(p->kv_len, p->q_tile) *
+                    sizeof(float));
+    w.total = off;
+  }
+  return w;
+}
+
+size_t workspace_bytes(const kascade_problem* p, int op) {
+  if (validate(p, op) != KASCADE_OK) return 0;
+  return is_decode(op) ? decode_workspace(p, op).total : prefill_workspace(p, op).total;
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+bool aligned4(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 3u) == 0; }
+
+int check_workspace(const kascade_problem* p, int op, void* ws, size_t ws_bytes) {
+  const size_t need = workspace_bytes(p, op);
+  if (need == 0) return KASCADE_OK;
+  if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0)
+    return KASCADE_ERR_WORKSPACE;
+  return KASCADE_OK;
+}
+
+float scale_log2(const kascade_problem* p) {
+  const float scale = p->scale > 0.0f ? p->scale : 1.0f / sqrtf((float)p->head_dim);
+  return scale * 1.4426950408889634f;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? KASCADE_OK : KASCADE_ERR_HIP; }
+
+#define KASCADE_TRY(expr)                   \
+  do {                                      \
+    const hipError_t e_ = (expr);           \
+    if (e_ != hipSuccess) return status_of(e_); \
+  } while (0)
+
+DecodeArgs decode_args(const kascade_problem* p, const void* q, const void* k, const void* v,
+                       const int32_t* idx, const DecodeWorkspace& w, char* ws) {
+  DecodeArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.idx = idx;
+  a.batch = p->batch;
+  a.hq = p->num_q_heads;
+  a.hkv = p->num_kv_heads;
+  a.group = p->num_q_heads / p->num_kv_heads;
+  a.n = p->kv_len;
+  a.d = p->head_dim;
+  a.keys_per_split = w.split.keys_per_split;
+  a.splits = w.split.splits;
+  a.scale_log2 = scale_log2(p);
+  a.part_ml = reinterpret_cast<float*>(ws + w.part_ml);
+  a.part_o = reinterpret_cast<float*>(ws + w.part_o);
+  a.logits = nullptr;
+  a.logits_ld = decode_logits_ld(p->kv_len);
+  return a;
+}
+
+PrefillArgs prefill_args(const kascade_problem* p, const void* q, const void* k, const void* v,
+                         const int32_t* idx, void* out) {
+  PrefillArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.idx = idx;
+  a.batch = p->batch;
+  a.hq = p->num_q_heads;
+  a.hkv = p->num_kv_heads;
+  a.group = p->num_q_heads / p->num_kv_heads;
+  a.n = p->kv_len;
+  a.d = p->head_dim;
+  a.tile = p->q_tile;
+  a.tiles = (p->kv_len + p->q_tile - 1) / p->q_tile;
+  a.topk = p->top_k;
+  a.scale_log2 = scale_log2(p);
+  a.out = static_cast<uint16_t*>(out);
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kascade_validate(const kascade_problem* p, int op) { return validate(p, op); }
+
+size_t kascade_workspace_bytes(const kascade_problem* p, int op) { return workspace_bytes(p, op); }
+
+const char* kascade_status_string(int status) {
+  switch (status) {
+    case KASCADE_OK: return "ok";
+    case KASCADE_ERR_INVALID: return "invalid argument";
+    case KASCADE_ERR_UNSUPPORTED: return "unsupported problem";
+    case KASCADE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case KASCADE_ERR_HIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+int kascade_anchor_decode(const kascade_problem* p, const void* q, const void* k, const void* v,
+                          void* out, int32_t* idx, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  int rc = validate(p, KASCADE_OP_ANCHOR_DECODE);
+  if (rc) return rc;
+  if (!q || !k || !idx || (out && !v)) return KASCADE_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || (v && !aligned16(v)) || (out && !aligned16(out)) ||
+      !aligned4(idx) || (lse && !aligned4(lse)))
+    return KASCADE_ERR_INVALID;
+  rc = check_workspace(p, KASCADE_OP_ANCHOR_DECODE, workspace, workspace_bytes);
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const DecodeWorkspace w = decode_workspace(p, KASCADE_OP_ANCHOR_DECODE);
+  char* ws = static_cast<char*>(workspace);
+  DecodeArgs a = decode_args(p, q, k, v, nullptr, w, ws);
+  a.list_len = p->kv_len;
+  a.logits = reinterpret_cast<float*>(ws + w.logits);
+  float* pooled = reinterpret_cast<float*>(ws + w.pooled);
+  const bool bf16 = p->dtype == KASCADE_BF16;
+  KASCADE_TRY(launch_decode_attn(a, bf16, false, out != nullptr, s));
+  KASCADE_TRY(launch_decode_pool(a.logits, a.part_ml, p->batch, a.hq, a.hkv, a.group, a.n,
+                                 a.splits, pooled, s));
+  KASCADE_TRY(launch_topk_decode(pooled, p->batch * a.hkv, a.n, p->top_k, idx, s));
+  if (out || lse)
+    KASCADE_TRY(launch_decode_combine(a.part_ml, a.part_o, p->batch * a.hq, a.splits, a.d, bf16,
+                                      out, lse, s));
+  return KASCADE_OK;
+}
+
+int kascade_reuse_decode(const kascade_problem* p, const void* q, const void* k, const void* v,
+                         const int32_t* idx, void* out, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  int rc = validate(p, KASCADE_OP_REUSE_DECODE);
+  if (rc) return rc;
+  if (!q || !k || !v || !idx || !out) return KASCADE_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned4(idx))
+    return KASCADE_ERR_INVALID;
+  rc = check_workspace(p, KASCADE_OP_REUSE_DECODE, workspace, workspace_bytes);
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const DecodeWorkspace w = decode_workspace(p, KASCADE_OP_REUSE_DECODE);
+  DecodeArgs a = decode_args(p, q, k, v, idx, w, static_cast<char*>(workspace));
+  a.list_len = p->top_k;
+  const bool bf16 = p->dtype == KASCADE_BF16;
+  KASCADE_TRY(launch_decode_attn(a, bf16, true, true, s));
+  KASCADE_TRY(launch_decode_combine(a.part_ml, a.part_o, p->batch * a.hq, a.splits, a.d, bf16, out,
+                                    nullptr, s));
+  return KASCADE_OK;
+}
+
+int kascade_anchor_prefill(const kascade_problem* p, const void* q, const void* k, const void* v,
+                           void* out, int32_t* idx, float* lse, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  int rc = validate(p, KASCADE_OP_ANCHOR_PREFILL);
+  if (rc) return rc;
+  if (!q || !k || !idx || (out && !v)) return KASCADE_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || (v && !aligned16(v)) || (out && !aligned16(out)) ||
+      !aligned4(idx) || (lse && !aligned4(lse)))
+    return KASCADE_ERR_INVALID;
+  rc = check_workspace(p, KASCADE_OP_ANCHOR_PREFILL, workspace, workspace_bytes);
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const PrefillWorkspace w = prefill_workspace(p, KASCADE_OP_ANCHOR_PREFILL);
+  char* ws = static_cast<char*>(workspace);
+  // Without a dense output only K is read; V is never touched.
+  PrefillArgs a = prefill_args(p, q, k, out ? v : k, nullptr, out);
+  a.lse2 = reinterpret_cast<float*>(ws + w.lse2);
+  a.pooled = reinterpret_cast<float*>(ws + w.pooled);
+  KASCADE_TRY(launch_prefill_dense(a, s));
+  KASCADE_TRY(launch_prefill_pool(a, s));
+  KASCADE_TRY(launch_topk_prefill(a.pooled, p->batch, a.hkv, a.n, a.tile, p->top_k, idx, s));
+  if (lse)
+    KASCADE_TRY(launch_lse2_to_lse(a.lse2, lse, (size_t)p->batch * a.hq * a.n, s));
+  return KASCADE_OK;
+}
+
+int kascade_reuse_prefill(const kascade_problem* p, const void* q, const void* k, const void* v,
+                          const int32_t* idx, void* out, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  int rc = validate(p, KASCADE_OP_REUSE_PREFILL);
+  if (rc) return rc;
+  if (!q || !k || !v || !idx || !out) return KASCADE_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned4(idx))
+    return KASCADE_ERR_INVALID;
+  rc = check_workspace(p, KASCADE_OP_REUSE_PREFILL, workspace, workspace_bytes);
+  if (rc) return rc;
+  PrefillArgs a = prefill_args(p, q, k, v, idx, out);
+  KASCADE_TRY(launch_prefill_reuse(a, static_cast<hipStream_t>(stream)));
+  return KASCADE_OK;
+}
+
+}  // extern "C"

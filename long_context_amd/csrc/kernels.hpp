@@ -1,0 +1,82 @@
+// Internal launch interface between the C ABI (kascade_api.hip) and the
+// kernels. Not installed; the public interface is include/kascade.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kascade {
+
+// ---- decode -----------------------------------------------------------------
+
+// One decode attention pass over a key list, split across wavefronts.
+// Dense mode walks keys 0..N-1; gather mode walks idx rows (entries -1 skipped).
+struct DecodeArgs {
+  const void* q;         // [B, Hq, 1, d]
+  const void* k;         // [B, Hkv, N, d]
+  const void* v;         // [B, Hkv, N, d] (only read when with_pv)
+  const int32_t* idx;    // gather mode: [B, Hkv, 1, list_len]
+  int batch, hq, hkv, group, n, list_len, d;
+  int keys_per_split, splits;
+  float scale_log2;      // logit scale times log2(e)
+  float* part_ml;        // [B*Hq*splits][2]: running max (log2 units) and sum
+  float* part_o;         // [B*Hq*splits][d]: unnormalised partial output
+  float* logits;         // dense mode, optional: [B, Hq, logits_ld] scaled logits, log2 units
+  int logits_ld;         // row stride of logits: N rounded up to a multiple of 4
+};
+
+__host__ __device__ inline int decode_logits_ld(int n) { return (n + 3) & ~3; }
+
+hipError_t launch_decode_attn(const DecodeArgs& a, bool bf16, bool gather, bool with_pv,
+                              hipStream_t s);
+
+// Merge split partials into the output row and/or the log-sum-exp.
+hipError_t launch_decode_combine(const float* part_ml, const float* part_o, int rows, int splits,
+                                 int d, bool bf16, void* out, float* lse, hipStream_t s);
+
+// pooled[b, kv, j] = sum over the group's heads of exp2(logit - lse2).
+hipError_t launch_decode_pool(const float* logits, const float* part_ml, int batch, int hq,
+                              int hkv, int group, int n, int splits, float* pooled,
+                              hipStream_t s);
+
+// ---- selection --------------------------------------------------------------
+
+// Exact top-k of non-negative float scores per segment, ascending indices,
+// lower index first among equal scores, -1 padding up to k.
+// Decode: segment s = (b, kv) covers scores[s*n .. s*n+n), writes idx[s*k ..].
+hipError_t launch_topk_decode(const float* scores, int segments, int n, int k, int32_t* idx,
+                              hipStream_t s);
+// Prefill: segment (b, kv, t) covers prefix_t = min((t+1)*T, N) scores stored
+// ragged: base (b*Hkv + kv) * ragged_len + T*t*(t+1)/2.
+hipError_t launch_topk_prefill(const float* scores, int batch, int hkv, int n, int tile, int k,
+                               int32_t* idx, hipStream_t s);
+
+// Elements of one (b, kv) ragged pooled row: tiles 0..tiles-2 are full and
+// hold (t+1)*tile candidates, the last one holds n; tile t starts at
+// tile*t*(t+1)/2.
+__host__ __device__ inline size_t prefill_ragged_len(int n, int tile) {
+  const size_t tiles = (size_t)(n + tile - 1) / tile;
+  return (size_t)tile * (tiles - 1) * tiles / 2 + (size_t)n;
+}
+
+// ---- prefill ----------------------------------------------------------------
+
+struct PrefillArgs {
+  const uint16_t* q;     // [B, Hq, N, d] bf16
+  const uint16_t* k;     // [B, Hkv, N, d]
+  const uint16_t* v;
+  const int32_t* idx;    // reuse: [B, Hkv, tiles, topk]
+  int batch, hq, hkv, group, n, d, tile, tiles, topk;
+  float scale_log2;
+  uint16_t* out;         // [B, Hq, N, d] bf16 (optional in the anchor)
+  float* lse2;           // [B, Hq, N] log2-domain log-sum-exp (anchor pass 1 output)
+  float* pooled;         // ragged pooled scores (anchor pass 2 output)
+};
+
+hipError_t launch_prefill_dense(const PrefillArgs& a, hipStream_t s);   // pass 1: lse2 (+ out)
+hipError_t launch_prefill_pool(const PrefillArgs& a, hipStream_t s);    // pass 2: pooled
+hipError_t launch_prefill_reuse(const PrefillArgs& a, hipStream_t s);   // reuse attention
+hipError_t launch_lse2_to_lse(const float* lse2, float* lse, size_t count, hipStream_t s);
+
+}  // namespace kascade

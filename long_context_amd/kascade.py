@@ -1,0 +1,209 @@
+"""ctypes binding of libkascade.so, the gfx950 library declared in include/kascade.h.
+
+Argument marshalling only: tensors are passed as device pointers and shapes,
+every step runs in the library's HIP kernels. There is no fallback; if the
+library has not been built, loading fails with an error.
+"""
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkascade.so")
+
+F32, BF16 = 0, 1
+OP_ANCHOR_DECODE, OP_REUSE_DECODE, OP_ANCHOR_PREFILL, OP_REUSE_PREFILL = 0, 1, 2, 3
+OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
+
+EXPORTS = ("kascade_validate", "kascade_workspace_bytes", "kascade_status_string",
+           "kascade_anchor_decode", "kascade_reuse_decode", "kascade_anchor_prefill",
+           "kascade_reuse_prefill")
+
+
+class KascadeError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(message)
+        self.status = status
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("q_len", ctypes.c_int32),
+        ("kv_len", ctypes.c_int32),
+        ("top_k", ctypes.c_int32),
+        ("q_tile", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+class Library:
+    def __init__(self, path=LIB_PATH):
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with `python -m long_context_amd.build` "
+                               "or __graft_entry__.build()")
+        self.path = path
+        lib = ctypes.CDLL(path)
+        P = ctypes.POINTER(Problem)
+        vp, sz = ctypes.c_void_p, ctypes.c_size_t
+        lib.kascade_validate.argtypes = [P, ctypes.c_int]
+        lib.kascade_validate.restype = ctypes.c_int
+        lib.kascade_workspace_bytes.argtypes = [P, ctypes.c_int]
+        lib.kascade_workspace_bytes.restype = sz
+        lib.kascade_status_string.argtypes = [ctypes.c_int]
+        lib.kascade_status_string.restype = ctypes.c_char_p
+        anchor = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        reuse = [P, vp, vp, vp, vp, vp, vp, sz, vp]
+        for name, args in (("kascade_anchor_decode", anchor), ("kascade_anchor_prefill", anchor),
+                           ("kascade_reuse_decode", reuse), ("kascade_reuse_prefill", reuse)):
+            f = getattr(lib, name)
+            f.argtypes = args
+            f.restype = ctypes.c_int
+        self.lib = lib
+
+    # -- host-only queries ------------------------------------------------------
+    def validate(self, prob, op):
+        return self.lib.kascade_validate(ctypes.byref(prob), op)
+
+    def workspace_bytes(self, prob, op):
+        return self.lib.kascade_workspace_bytes(ctypes.byref(prob), op)
+
+    def status_string(self, status):
+        return self.lib.kascade_status_string(status).decode()
+
+    def check(self, status, what):
+        if status != OK:
+            raise KascadeError(status, f"{what}: {self.status_string(status)} ({status})")
+
+    # -- raw entry points (integer device addresses, 0 = NULL) -------------------
+    def anchor_decode_raw(self, prob, q, k, v, out, idx, lse, ws, ws_bytes, stream):
+        return self.lib.kascade_anchor_decode(ctypes.byref(prob), q, k, v, out, idx, lse, ws,
+                                              ws_bytes, stream)
+
+    def reuse_decode_raw(self, prob, q, k, v, idx, out, ws, ws_bytes, stream):
+        return self.lib.kascade_reuse_decode(ctypes.byref(prob), q, k, v, idx, out, ws, ws_bytes,
+                                             stream)
+
+    def anchor_prefill_raw(self, prob, q, k, v, out, idx, lse, ws, ws_bytes, stream):
+        return self.lib.kascade_anchor_prefill(ctypes.byref(prob), q, k, v, out, idx, lse, ws,
+                                               ws_bytes, stream)
+
+    def reuse_prefill_raw(self, prob, q, k, v, idx, out, ws, ws_bytes, stream):
+        return self.lib.kascade_reuse_prefill(ctypes.byref(prob), q, k, v, idx, out, ws, ws_bytes,
+                                              stream)
+
+
+_library = None
+
+
+def library():
+    global _library
+    if _library is None:
+        _library = Library()
+    return _library
+
+
+# ---- tensor-level wrappers ---------------------------------------------------
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def problem(q, k, top_k, q_tile=128, scale=0.0):
+    """Problem descriptor from Q [B,Hq,L,d] and K [B,Hkv,N,d]."""
+    B, Hq, L, d = q.shape
+    Bk, Hkv, N, dk = k.shape
+    if Bk != B or dk != d:
+        raise ValueError(f"shape mismatch q {tuple(q.shape)} k {tuple(k.shape)}")
+    return Problem(B, Hq, Hkv, d, L, N, int(top_k), int(q_tile), float(scale), _dtype_code(q))
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def workspace(prob, op, device):
+    """A workspace tensor of kascade_workspace_bytes() bytes (None if zero)."""
+    n = library().workspace_bytes(prob, op)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def _ws(ws):
+    return (None, 0) if ws is None else (ws.data_ptr(), ws.numel())
+
+
+def anchor_decode(q, k, v, top_k, out=None, lse=None, idx=None, ws=None, scale=0.0, stream=None):
+    """Anchor decode; returns idx [B,Hkv,1,k] int32 (and fills out/lse if given)."""
+    lib = library()
+    prob = problem(q, k, top_k, 1, scale)
+    B, Hkv = k.shape[0], k.shape[1]
+    if idx is None:
+        idx = torch.empty((B, Hkv, 1, top_k), dtype=torch.int32, device=q.device)
+    if ws is None:
+        ws = workspace(prob, OP_ANCHOR_DECODE, q.device)
+    wp, wb = _ws(ws)
+    lib.check(lib.anchor_decode_raw(prob, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(idx), _ptr(lse),
+                                    wp, wb, _stream(stream)), "kascade_anchor_decode")
+    return idx
+
+
+def reuse_decode(q, k, v, idx, out=None, ws=None, scale=0.0, stream=None):
+    """Reuse decode over idx [B,Hkv,1,k]; returns out [B,Hq,1,d]."""
+    lib = library()
+    prob = problem(q, k, idx.shape[-1], 1, scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if ws is None:
+        ws = workspace(prob, OP_REUSE_DECODE, q.device)
+    wp, wb = _ws(ws)
+    lib.check(lib.reuse_decode_raw(prob, _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(out), wp, wb,
+                                   _stream(stream)), "kascade_reuse_decode")
+    return out
+
+
+def anchor_prefill(q, k, v, top_k, q_tile=128, out=None, lse=None, idx=None, ws=None, scale=0.0,
+                   stream=None):
+    """Anchor causal prefill; returns idx [B,Hkv,ceil(N/T),k] int32."""
+    lib = library()
+    prob = problem(q, k, top_k, q_tile, scale)
+    B, Hkv, N = k.shape[0], k.shape[1], k.shape[2]
+    if idx is None:
+        idx = torch.empty((B, Hkv, -(-N // q_tile), top_k), dtype=torch.int32, device=q.device)
+    if ws is None:
+        ws = workspace(prob, OP_ANCHOR_PREFILL, q.device)
+    wp, wb = _ws(ws)
+    lib.check(lib.anchor_prefill_raw(prob, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(idx), _ptr(lse),
+                                     wp, wb, _stream(stream)), "kascade_anchor_prefill")
+    return idx
+
+
+def reuse_prefill(q, k, v, idx, q_tile=128, out=None, ws=None, scale=0.0, stream=None):
+    """Reuse causal prefill over idx [B,Hkv,tiles,k]; returns out [B,Hq,N,d]."""
+    lib = library()
+    prob = problem(q, k, idx.shape[-1], q_tile, scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if ws is None:
+        ws = workspace(prob, OP_REUSE_PREFILL, q.device)
+    wp, wb = _ws(ws)
+    lib.check(lib.reuse_prefill_raw(prob, _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(out), wp, wb,
+                                    _stream(stream)), "kascade_reuse_prefill")
+    return out

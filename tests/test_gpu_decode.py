@@ -1,0 +1,168 @@
+"""Decode parity: the HIP library against the fp64 oracle, through the C ABI."""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+from parity import (check_close, check_index_band, check_lse, host64, log,  # noqa: E402
+                    random_index_sets)
+
+from long_context_amd import kascade as K  # noqa: E402
+from long_context_amd import synth  # noqa: E402
+from long_context_amd.synth import to_oracle  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _small(name, **kw):
+    base = dict(name=name, wid=900, phase="decode", batch=2, hq=8, hkv=2, d=128, n=4133, k=256,
+                tile=1, dtype="bf16", layers=2, planted=16, share=0.7)
+    base.update(kw)
+    return synth.Workload(**base)
+
+
+CASES = {
+    "decode_f32_1k": synth.WORKLOADS["decode_f32_1k"],
+    "bf16_d128_ragged": _small("bf16_d128_ragged"),
+    "bf16_d64_g8": _small("bf16_d64_g8", wid=901, hq=16, hkv=2, d=64, n=2000, k=100),
+    "f32_d128_g2": _small("f32_d128_g2", wid=902, hq=4, hkv=2, dtype="f32", n=777, k=65),
+    "bf16_g1": _small("bf16_g1", wid=903, hq=4, hkv=4, n=1500, k=129),
+    "bf16_g16": _small("bf16_g16", wid=904, hq=16, hkv=1, n=3000, k=300, batch=1),
+    "bf16_k_eq_n": _small("bf16_k_eq_n", wid=905, n=640, k=640),
+    "bf16_tiny": _small("bf16_tiny", wid=906, n=5, k=3, planted=1, batch=1),
+    "bf16_n1": _small("bf16_n1", wid=907, n=1, k=1, planted=0, batch=1),
+}
+
+
+def _layers(w):
+    """Anchor and first reuse layer, drawn on the CPU and copied to the GPU."""
+    stack = synth.make_stack(w.scaled(layers=2), device="cpu")
+    return stack[0], stack[1]
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_decode_anchor_and_reuse(lib, orc, case):
+    w = CASES[case]
+    log(f"[decode] case={case} B={w.batch} Hq={w.hq} Hkv={w.hkv} d={w.d} N={w.n} k={w.k} {w.dtype}")
+    (q0, k0, v0), (q1, k1, v1) = _layers(w)
+    dt = w.torch_dtype
+    # ---- anchor layer -------------------------------------------------------
+    qd, kd, vd = q0.to(DEV), k0.to(DEV), v0.to(DEV)
+    out = torch.empty_like(qd)
+    lse = torch.empty((w.batch, w.hq, 1), dtype=torch.float32, device=DEV)
+    idx = K.anchor_decode(qd, kd, vd, w.k, out=out, lse=lse)
+    torch.cuda.synchronize()
+    idx_o, pooled_o = orc.anchor_decode(to_oracle(q0), to_oracle(k0), w.k)
+    dense_o, lse_o = orc.dense(to_oracle(q0), to_oracle(k0), to_oracle(v0), causal=False)
+    gi = idx.cpu().numpy().reshape(-1, w.k)
+    same = [check_index_band(gi[u], idx_o[u], pooled_o[u], w.k, w.n, f"{case} unit {u}")
+            for u in range(gi.shape[0])]
+    check_close(host64(out).reshape(-1, w.d), dense_o, dt, f"{case} anchor dense out")
+    check_lse(host64(lse).reshape(-1), lse_o, f"{case} anchor lse")
+    if w.k == w.n:
+        assert np.array_equal(gi, np.tile(np.arange(w.n, dtype=np.int32), (gi.shape[0], 1)))
+    # ---- reuse layer, oracle's index sets -------------------------------------
+    idx_o4 = idx_o.reshape(w.batch, w.hkv, 1, w.k)
+    q1d, k1d, v1d = q1.to(DEV), k1.to(DEV), v1.to(DEV)
+    out_r = K.reuse_decode(q1d, k1d, v1d, torch.from_numpy(idx_o4).to(DEV))
+    torch.cuda.synchronize()
+    ref_r = orc.reuse_decode(to_oracle(q1), to_oracle(k1), to_oracle(v1), idx_o4)
+    check_close(host64(out_r).reshape(-1, w.d), ref_r, dt, f"{case} reuse out")
+    # ---- chained: GPU anchor indices feed the GPU reuse ----------------------
+    out_c = K.reuse_decode(q1d, k1d, v1d, idx)
+    torch.cuda.synchronize()
+    G = w.hq // w.hkv
+    for u, s in enumerate(same):
+        if s:
+            rows = slice(u * G, (u + 1) * G)
+            check_close(host64(out_c).reshape(-1, w.d)[rows], ref_r[rows], dt, f"{case} chain unit {u}")
+
+
+def test_decode_reuse_padding_anywhere(lib, orc):
+    """-1 entries are skipped wherever they sit; an all -1 list gives zeros."""
+    w = _small("pad", wid=910, n=1000, k=96)
+    log("[decode] case=padding_anywhere")
+    (q, k, v), _ = _layers(w)
+    rng = np.random.default_rng(3)
+    idx = random_index_sets(rng, (w.batch, w.hkv, 1), w.n, w.k)
+    idx[0, 0, 0, rng.choice(w.k, 30, replace=False)] = -1
+    idx[1, 1, 0, :] = -1
+    out = K.reuse_decode(q.to(DEV), k.to(DEV), v.to(DEV), torch.from_numpy(idx).to(DEV))
+    torch.cuda.synchronize()
+    ref = orc.reuse_decode(to_oracle(q), to_oracle(k), to_oracle(v), idx)
+    check_close(host64(out).reshape(-1, w.d), ref, torch.bfloat16, "padding")
+    assert np.all(host64(out)[1, 4:8] == 0.0)
+
+
+def test_decode_ties_go_to_lower_index(lib):
+    """All keys identical: every pooled score ties, the first k keys win."""
+    log("[decode] case=ties")
+    B, Hq, Hkv, d, N, k = 1, 4, 1, 128, 700, 50
+    g = torch.Generator().manual_seed(11)
+    q = torch.randn((B, Hq, 1, d), generator=g).to(torch.bfloat16)
+    row = torch.randn((1, 1, 1, d), generator=g).to(torch.bfloat16)
+    kk = row.expand(B, Hkv, N, d).contiguous()
+    idx = K.anchor_decode(q.to(DEV), kk.to(DEV), None, k)
+    torch.cuda.synchronize()
+    assert idx.cpu().numpy().reshape(-1).tolist() == list(range(k))
+
+
+def test_decode_deterministic(lib):
+    w = _small("det", wid=911)
+    log("[decode] case=determinism")
+    (q, k, v), _ = _layers(w)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    a = [K.anchor_decode(qd, kd, vd, w.k) for _ in range(2)]
+    o = [K.reuse_decode(qd, kd, vd, a[0]) for _ in range(2)]
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], a[1]) and torch.equal(o[0], o[1])
+
+
+def _sampled_full(orc, w, units, seed):
+    """Full-size decode workload, drawn on the GPU; oracle checks on sampled (b, kv)."""
+    pos = synth.planted_positions(w.scaled(layers=2))
+    q0, k0, v0 = synth.make_layer(w, 0, DEV, pos)
+    q1, k1, v1 = synth.make_layer(w, 1, DEV, pos)
+    G = w.group
+    out = torch.empty_like(q0)
+    lse = torch.empty((w.batch, w.hq, 1), dtype=torch.float32, device=DEV)
+    idx = K.anchor_decode(q0, k0, v0, w.k, out=out, lse=lse)
+    torch.cuda.synchronize()
+    gi = idx.cpu().numpy()
+    out_h, lse_h = host64(out), host64(lse)
+    rng = np.random.default_rng(seed)
+    idx_r = random_index_sets(rng, (w.batch, w.hkv, 1), w.n, w.k)
+    refs = {}
+    for (b, kv) in units:
+        qs, ks, vs = (to_oracle(q0[b:b + 1, kv * G:(kv + 1) * G]), to_oracle(k0[b:b + 1, kv:kv + 1]),
+                      to_oracle(v0[b:b + 1, kv:kv + 1]))
+        io, po = orc.anchor_decode(qs, ks, w.k)
+        check_index_band(gi[b, kv, 0], io[0], po[0], w.k, w.n, f"{w.name} anchor ({b},{kv})")
+        do, lo = orc.dense(qs, ks, vs, causal=False)
+        check_close(out_h[b, kv * G:(kv + 1) * G, 0], do, w.torch_dtype, f"{w.name} dense ({b},{kv})")
+        check_lse(lse_h[b, kv * G:(kv + 1) * G, 0], lo, f"{w.name} lse ({b},{kv})")
+        idx_r[b, kv, 0] = io[0]
+        refs[(b, kv)] = (io[0], (to_oracle(q1[b:b + 1, kv * G:(kv + 1) * G]),
+                                 to_oracle(k1[b:b + 1, kv:kv + 1]), to_oracle(v1[b:b + 1, kv:kv + 1])))
+    out_r = K.reuse_decode(q1, k1, v1, torch.from_numpy(idx_r).to(DEV))
+    torch.cuda.synchronize()
+    out_rh = host64(out_r)
+    for (b, kv), (io, (qs, ks, vs)) in refs.items():
+        ro = orc.reuse_decode(qs, ks, vs, io.reshape(1, 1, 1, -1))
+        check_close(out_rh[b, kv * G:(kv + 1) * G, 0], ro, w.torch_dtype, f"{w.name} reuse ({b},{kv})")
+
+
+def test_decode_llama8b_32k_sampled(lib, orc):
+    w = synth.WORKLOADS["decode_llama8b_32k"]
+    log("[decode] case=decode_llama8b_32k full size, sampled units")
+    _sampled_full(orc, w, [(0, 0), (5, 3), (11, 6), (15, 7)], seed=21)
+
+
+def test_decode_128k_sampled(lib, orc):
+    w = synth.WORKLOADS["decode_128k"]
+    log("[decode] case=decode_128k full size, sampled units")
+    _sampled_full(orc, w, [(0, 0), (1, 5), (3, 7)], seed=22)
