@@ -1,0 +1,291 @@
+"""Benchmark of the Kascade hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+  * decode at 32K context, Llama-3-8B attention shape (B=16, Hq=32, Hkv=8,
+    d=128, k=2048, bf16): one anchor layer (dense scores, pooled top-k, dense
+    output) and three reuse layers with their own K/V;
+  * causal prefill at 8K (B=1, Hq=32, Hkv=8, d=128, T=128, k=1024, bf16): one
+    anchor layer (row log-sum-exp and dense output, pooled tile scores, per
+    tile top-k) and three reuse layers.
+All inputs are resident in HBM before timing starts. Prints one JSON line.
+
+value = decode attention microseconds per layer (mean of the four decode
+layers); the decode reuse-layer HBM rate and the prefill tokens/s sit beside it.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+from long_context_amd import kascade as K
+from long_context_amd import synth
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, vendor figure
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores, vendor figure
+
+METRIC = "decode attn µs/layer + HBM GB/s at 32K ctx; prefill attn tokens/s at 8K"
+
+
+def bytes_of(*ts):
+    return sum(t.numel() * t.element_size() for t in ts)
+
+
+class DecodeStack:
+    def __init__(self, w, dev):
+        self.w = w
+        pos = synth.planted_positions(w)
+        self.layers = [synth.make_layer(w, l, dev, pos) for l in range(w.layers)]
+        q0, k0, v0 = self.layers[0]
+        self.out = [torch.empty_like(q) for q, _, _ in self.layers]
+        self.lse = torch.empty((w.batch, w.hq, 1), dtype=torch.float32, device=dev)
+        self.idx = torch.empty((w.batch, w.hkv, 1, w.k), dtype=torch.int32, device=dev)
+        self.ws_a = K.workspace(K.problem(q0, k0, w.k, 1), K.OP_ANCHOR_DECODE, dev)
+        self.ws_r = K.workspace(K.problem(q0, k0, w.k, 1), K.OP_REUSE_DECODE, dev)
+
+    def run(self, marks=None):
+        q, k, v = self.layers[0]
+        K.anchor_decode(q, k, v, self.w.k, out=self.out[0], lse=self.lse, idx=self.idx, ws=self.ws_a)
+        if marks is not None:
+            marks.append(("decode_anchor", _record()))
+        for l in range(1, len(self.layers)):
+            q, k, v = self.layers[l]
+            K.reuse_decode(q, k, v, self.idx, out=self.out[l], ws=self.ws_r)
+            if marks is not None:
+                marks.append(("decode_reuse", _record()))
+
+    def reuse_bytes(self):
+        """Algorithmic bytes of one reuse layer: gathered K and V rows, idx, Q and O."""
+        w = self.w
+        rows = w.batch * w.hkv * w.k
+        q, _, _ = self.layers[1]
+        return rows * w.d * 2 * 2 + self.idx.numel() * 4 + 2 * bytes_of(q)
+
+    def anchor_bytes(self):
+        """Algorithmic bytes of the anchor: K and V read once (dense output requested)."""
+        _, k, v = self.layers[0]
+        return bytes_of(k, v)
+
+
+class PrefillStack:
+    def __init__(self, w, dev):
+        self.w = w
+        pos = synth.planted_positions(w)
+        self.layers = [synth.make_layer(w, l, dev, pos) for l in range(w.layers)]
+        q0, k0, _ = self.layers[0]
+        self.out = [torch.empty_like(q) for q, _, _ in self.layers]
+        self.idx = torch.empty((w.batch, w.hkv, w.tiles, w.k), dtype=torch.int32, device=dev)
+        self.ws_a = K.workspace(K.problem(q0, k0, w.k, w.tile), K.OP_ANCHOR_PREFILL, dev)
+
+    def run(self, marks=None):
+        q, k, v = self.layers[0]
+        K.anchor_prefill(q, k, v, self.w.k, self.w.tile, out=self.out[0], idx=self.idx, ws=self.ws_a)
+        if marks is not None:
+            marks.append(("prefill_anchor", _record()))
+        for l in range(1, len(self.layers)):
+            q, k, v = self.layers[l]
+            K.reuse_prefill(q, k, v, self.idx, self.w.tile, out=self.out[l])
+            if marks is not None:
+                marks.append(("prefill_reuse", _record()))
+
+    def qk_flops(self):
+        """Tile-granular causal QK^T flops of one pass over the sequence:
+        every tile's G*T rows against its whole prefix of keys."""
+        w = self.w
+        total = 0
+        for t in range(w.tiles):
+            rows = min(w.tile, w.n - t * w.tile)
+            total += w.batch * w.hq * rows * min((t + 1) * w.tile, w.n) * 2 * w.d
+        return total
+
+    def reuse_flops(self):
+        """Tile-granular QK^T plus PV flops of one reuse layer over the saved sets."""
+        w = self.w
+        total = 0
+        for t in range(w.tiles):
+            rows = min(w.tile, w.n - t * w.tile)
+            total += w.batch * w.hq * rows * min(w.k, (t + 1) * w.tile, w.n) * 2 * w.d * 2
+        return total
+
+
+def _record():
+    e = torch.cuda.Event(enable_timing=True)
+    e.record()
+    return e
+
+
+def cpu_baseline(dec, threads, budget_s=20.0):
+    """The fp64 oracle on a bounded sample of the decode step, scaled to us/layer."""
+    import oracle
+    orc = oracle.default()
+    w = dec.w
+    G = w.group
+    rng = np.random.default_rng(7)
+    units = [(int(b), int(kv)) for b, kv in zip(rng.integers(0, w.batch, 64), rng.integers(0, w.hkv, 64))]
+    q0, k0, v0 = dec.layers[0]
+    t_anchor, n_anchor = 0.0, 0
+    start = time.time()
+    for (b, kv) in units:
+        qs = synth.to_oracle(q0[b:b + 1, kv * G:(kv + 1) * G])
+        ks = synth.to_oracle(k0[b:b + 1, kv:kv + 1])
+        vs = synth.to_oracle(v0[b:b + 1, kv:kv + 1])
+        t0 = time.perf_counter()
+        orc.anchor_decode(qs, ks, w.k, threads=threads, want_pooled=False)
+        orc.dense(qs, ks, vs, causal=False, threads=threads)
+        t_anchor += time.perf_counter() - t0
+        n_anchor += 1
+        if time.time() - start > budget_s / 2:
+            break
+    anchor_layer = t_anchor / n_anchor * (w.batch * w.hkv)
+    # reuse: whole (b, kv) units of the first reuse layer with the saved sets
+    q1, k1, v1 = dec.layers[1]
+    idx = dec.idx.cpu().numpy()
+    t_reuse, n_reuse = 0.0, 0
+    start = time.time()
+    for (b, kv) in units:
+        qs = synth.to_oracle(q1[b:b + 1, kv * G:(kv + 1) * G])
+        ks = synth.to_oracle(k1[b:b + 1, kv:kv + 1])
+        vs = synth.to_oracle(v1[b:b + 1, kv:kv + 1])
+        t0 = time.perf_counter()
+        orc.reuse_decode(qs, ks, vs, idx[b:b + 1, kv:kv + 1], threads=threads)
+        t_reuse += time.perf_counter() - t0
+        n_reuse += 1
+        if time.time() - start > budget_s / 2:
+            break
+    reuse_layer = t_reuse / n_reuse * (w.batch * w.hkv)
+    us_per_layer = (anchor_layer + (w.layers - 1) * reuse_layer) / w.layers * 1e6
+    return {"value": us_per_layer, "unit": "us/layer", "cores": threads, "kind": "oracle",
+            "sample": (f"decode 32K: {n_anchor} of {w.batch * w.hkv} (batch, KV head) units of the "
+                       f"anchor layer (scores, pooled top-k, dense output) and {n_reuse} units of one "
+                       "reuse layer, timed and scaled to whole layers")}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(see the sharding notes in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = "cuda"
+    lib = K.library()
+    dec = DecodeStack(synth.WORKLOADS["decode_llama8b_32k"], dev)
+    pre = PrefillStack(synth.WORKLOADS["prefill_8k"], dev)
+    torch.cuda.synchronize()
+
+    def step(marks=None):
+        dec.run(marks)
+        pre.run(marks)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, per-call marks on the current stream, per-kernel
+    # events inside the library
+    lib.timing_collect()
+    lib.timing_enable(True)
+    marks = []
+    start = _record()
+    for _ in range(args.steps):
+        marks.append(("step_start", _record()))
+        step(marks)
+    stop = _record()
+    torch.cuda.synchronize()
+    lib.timing_enable(False)
+    kernels = lib.timing_collect()
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / args.steps
+
+    calls = {}
+    prev = None
+    for name, ev in marks:
+        if prev is not None and name != "step_start":
+            calls.setdefault(name, []).append(prev.elapsed_time(ev))
+        prev = ev
+    avg = {n: float(np.mean(v)) for n, v in calls.items()}
+    kern = {n: (ms / cnt) for n, (ms, cnt) in kernels.items()}
+
+    wd, wp = dec.w, pre.w
+    t_dec_layer_ms = (avg["decode_anchor"] + (wd.layers - 1) * avg["decode_reuse"]) / wd.layers
+    t_pre_stack_ms = avg["prefill_anchor"] + (wp.layers - 1) * avg["prefill_reuse"]
+    prefill_tps = wp.batch * wp.n * wp.layers / (t_pre_stack_ms * 1e-3)
+    reuse_gbs = dec.reuse_bytes() / (kern["decode_attn_gather"] * 1e-3) / 1e9
+    reuse_call_gbs = dec.reuse_bytes() / (avg["decode_reuse"] * 1e-3) / 1e9
+    anchor_gbs = dec.anchor_bytes() / (kern["decode_attn_dense"] * 1e-3) / 1e9
+    pool_tflops = pre.qk_flops() / (kern["prefill_pool"] * 1e-3) / 1e12
+    dense_tflops = 2 * pre.qk_flops() / (kern["prefill_dense"] * 1e-3) / 1e12
+    gather_tflops = pre.reuse_flops() / (kern["prefill_gather"] * 1e-3) / 1e12
+
+    # dominant kernel: the largest share of the step
+    per_step = {n: kernels[n][0] / args.steps for n in kernels}
+    dominant = max(per_step, key=per_step.get)
+    rooflines = {
+        "decode_attn_dense": ("hbm", anchor_gbs, PEAK_HBM_GBS, "GB/s", dec.anchor_bytes()),
+        "decode_attn_gather": ("hbm", reuse_gbs, PEAK_HBM_GBS, "GB/s", dec.reuse_bytes()),
+        "prefill_pool": ("mfma", pool_tflops, PEAK_BF16_TFLOPS, "TFLOP/s", pre.qk_flops()),
+        "prefill_dense": ("mfma", dense_tflops, PEAK_BF16_TFLOPS, "TFLOP/s", 2 * pre.qk_flops()),
+        "prefill_gather": ("mfma", gather_tflops, PEAK_BF16_TFLOPS, "TFLOP/s", pre.reuse_flops()),
+    }
+    bound, achieved, peak, unit, work = rooflines.get(dominant, rooflines["decode_attn_dense"])
+    roofline = {"kernel": dominant, "bound": bound, "achieved": round(achieved, 2), "peak": peak,
+                "unit": unit, "frac": round(achieved / peak, 4), "traffic": None,
+                "work_per_launch": work, "avg_launch_ms": round(kern[dominant], 5)}
+
+    result = {
+        "metric": METRIC,
+        "value": round(t_dec_layer_ms * 1e3, 3),
+        "unit": "us/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode_llama8b_32k (anchor + 3 reuse layers) + prefill_8k (anchor + 3 reuse layers)",
+            "decode": {"batch": wd.batch, "hq": wd.hq, "hkv": wd.hkv, "d": wd.d, "context": wd.n, "top_k": wd.k},
+            "prefill": {"batch": wp.batch, "hq": wp.hq, "hkv": wp.hkv, "d": wp.d, "seq_len": wp.n,
+                        "q_tile": wp.tile, "top_k": wp.k},
+        },
+        "roofline": roofline,
+        "metrics": {
+            "decode_us_per_layer": round(t_dec_layer_ms * 1e3, 3),
+            "decode_anchor_us": round(avg["decode_anchor"] * 1e3, 2),
+            "decode_reuse_us": round(avg["decode_reuse"] * 1e3, 2),
+            "decode_reuse_hbm_gbs_kernel": round(reuse_gbs, 1),
+            "decode_reuse_hbm_gbs_call": round(reuse_call_gbs, 1),
+            "decode_anchor_hbm_gbs_kernel": round(anchor_gbs, 1),
+            "prefill_tokens_per_s": round(prefill_tps, 1),
+            "prefill_anchor_us": round(avg["prefill_anchor"] * 1e3, 2),
+            "prefill_reuse_us": round(avg["prefill_reuse"] * 1e3, 2),
+            "prefill_pool_tflops": round(pool_tflops, 2),
+            "prefill_dense_tflops": round(dense_tflops, 2),
+            "prefill_gather_tflops": round(gather_tflops, 2),
+            "kernel_avg_us": {n: round(v * 1e3, 2) for n, v in sorted(kern.items())},
+            "rooflines": {n: {"bound": r[0], "achieved": round(r[1], 2), "peak": r[2], "unit": r[3],
+                              "frac": round(r[1] / r[2], 4)} for n, r in rooflines.items()},
+        },
+    }
+    if not args.no_cpu_baseline:
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+        result["cpu_baseline"] = cpu_baseline(dec, threads, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -109,9 +109,9 @@ int kascade_anchor_decode(const kascade_problem* p, const void* q, const void* k
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* Reuse layer, decode. For each (b, h): softmax attention of q over the keys
- * idx[b, h/G, 0, :] (entries -1 skipped) with this layer's K and V, written to
- * out [B, Hq, 1, d]. An entry outside [-1, N) is a caller error whose result
- * is unspecified. */
+ * idx[b, h/G, 0, :] with this layer's K and V, written to out [B, Hq, 1, d].
+ * Entries -1 (and any entry outside [0, N)) are skipped; a row whose list has
+ * no usable entry gets zeros. */
 int kascade_reuse_decode(const kascade_problem* p, const void* q, const void* k,
                          const void* v, const int32_t* idx, void* out,
                          void* workspace, size_t workspace_bytes, void* stream);
@@ -126,14 +126,32 @@ int kascade_anchor_prefill(const kascade_problem* p, const void* q, const void* 
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* Reuse layer, causal prefill. Row i of tile t attends to the keys
- * j in idx[b, h/G, t, :] with j != -1 and j <= i; a row with no such key gets
- * zeros. Output out [B, Hq, N, d]. */
+ * j in idx[b, h/G, t, 0:k_t] with 0 <= j <= i (entries -1, or outside the
+ * sequence, are skipped); a row with no such key gets zeros. Output
+ * out [B, Hq, N, d]. Slots at or past k_t = min(k, prefix_t) are not read. */
 int kascade_reuse_prefill(const kascade_problem* p, const void* q, const void* k,
                           const void* v, const int32_t* idx, void* out,
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static text for a status code. */
 const char* kascade_status_string(int status);
+
+/* ---- optional per-kernel timing (tracing) ----------------------------------
+ * While enabled, every kernel the library enqueues is bracketed by a pair of
+ * HIP events recorded on the call's stream. kascade_timing_collect() waits
+ * for the recorded events, adds their elapsed times per kernel name into
+ * out[0..max_entries) and clears the record. Timing is process-wide and off
+ * by default; the events are created by the library on first use and reused.
+ * kascade_timing_enable returns the previous setting. kascade_timing_collect
+ * returns the number of entries written, or -1 on a HIP error. */
+typedef struct {
+  char name[40];       /* kernel name, NUL-terminated */
+  double total_ms;     /* summed duration of its launches */
+  int64_t launches;    /* number of launches summed */
+} kascade_kernel_time;
+
+int kascade_timing_enable(int on);
+int kascade_timing_collect(kascade_kernel_time* out, int max_entries);
 
 #ifdef __cplusplus
 }

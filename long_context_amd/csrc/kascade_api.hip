@@ -4,6 +4,9 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+#include <vector>
+
 #include "kascade.h"
 #include "kernels.hpp"
 
@@ -129,10 +132,57 @@ float scale_log2(const kascade_problem* p) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? KASCADE_OK : KASCADE_ERR_HIP; }
 
-#define KASCADE_TRY(expr)                   \
-  do {                                      \
-    const hipError_t e_ = (expr);           \
-    if (e_ != hipSuccess) return status_of(e_); \
+// ---- optional per-kernel timing ---------------------------------------------
+
+struct TimedLaunch {
+  const char* name;
+  hipEvent_t start, stop;
+};
+
+struct Timing {
+  std::mutex mu;
+  bool on = false;
+  std::vector<TimedLaunch> pending;
+  std::vector<hipEvent_t> spare;
+
+  hipEvent_t event() {
+    if (!spare.empty()) {
+      hipEvent_t e = spare.back();
+      spare.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    return hipEventCreate(&e) == hipSuccess ? e : nullptr;
+  }
+};
+
+Timing& timing() {
+  static Timing t;
+  return t;
+}
+
+// Run one launch; when timing is on, bracket it with events on its stream.
+template <class F>
+hipError_t timed(const char* name, hipStream_t s, F&& launch) {
+  Timing& t = timing();
+  std::unique_lock<std::mutex> lock(t.mu);
+  if (!t.on) {
+    lock.unlock();
+    return launch();
+  }
+  hipEvent_t a = t.event(), b = t.event();
+  if (!a || !b) return hipErrorOutOfMemory;
+  hipError_t e = hipEventRecord(a, s);
+  if (e == hipSuccess) e = launch();
+  if (e == hipSuccess) e = hipEventRecord(b, s);
+  t.pending.push_back({name, a, b});
+  return e;
+}
+
+#define KASCADE_TRY(name, expr)                                   \
+  do {                                                            \
+    const hipError_t e_ = timed(name, s, [&] { return (expr); }); \
+    if (e_ != hipSuccess) return status_of(e_);                   \
   } while (0)
 
 DecodeArgs decode_args(const kascade_problem* p, const void* q, const void* k, const void* v,
@@ -217,13 +267,13 @@ int kascade_anchor_decode(const kascade_problem* p, const void* q, const void* k
   a.logits = reinterpret_cast<float*>(ws + w.logits);
   float* pooled = reinterpret_cast<float*>(ws + w.pooled);
   const bool bf16 = p->dtype == KASCADE_BF16;
-  KASCADE_TRY(launch_decode_attn(a, bf16, false, out != nullptr, s));
-  KASCADE_TRY(launch_decode_pool(a.logits, a.part_ml, p->batch, a.hq, a.hkv, a.group, a.n,
+  KASCADE_TRY("decode_attn_dense", launch_decode_attn(a, bf16, false, out != nullptr, s));
+  KASCADE_TRY("decode_pool", launch_decode_pool(a.logits, a.part_ml, p->batch, a.hq, a.hkv, a.group, a.n,
                                  a.splits, pooled, s));
-  KASCADE_TRY(launch_topk_decode(pooled, p->batch * a.hkv, a.n, p->top_k, idx, s));
+  KASCADE_TRY("topk_decode", launch_topk_decode(pooled, p->batch * a.hkv, a.n, p->top_k, idx, s));
   if (out || lse)
-    KASCADE_TRY(launch_decode_combine(a.part_ml, a.part_o, p->batch * a.hq, a.splits, a.d, bf16,
-                                      out, lse, s));
+    KASCADE_TRY("decode_combine", launch_decode_combine(a.part_ml, a.part_o, p->batch * a.hq,
+                                                        a.splits, a.d, bf16, out, lse, s));
   return KASCADE_OK;
 }
 
@@ -242,9 +292,9 @@ int kascade_reuse_decode(const kascade_problem* p, const void* q, const void* k,
   DecodeArgs a = decode_args(p, q, k, v, idx, w, static_cast<char*>(workspace));
   a.list_len = p->top_k;
   const bool bf16 = p->dtype == KASCADE_BF16;
-  KASCADE_TRY(launch_decode_attn(a, bf16, true, true, s));
-  KASCADE_TRY(launch_decode_combine(a.part_ml, a.part_o, p->batch * a.hq, a.splits, a.d, bf16, out,
-                                    nullptr, s));
+  KASCADE_TRY("decode_attn_gather", launch_decode_attn(a, bf16, true, true, s));
+  KASCADE_TRY("decode_combine", launch_decode_combine(a.part_ml, a.part_o, p->batch * a.hq,
+                                                      a.splits, a.d, bf16, out, nullptr, s));
   return KASCADE_OK;
 }
 
@@ -266,11 +316,11 @@ int kascade_anchor_prefill(const kascade_problem* p, const void* q, const void* 
   PrefillArgs a = prefill_args(p, q, k, out ? v : k, nullptr, out);
   a.lse2 = reinterpret_cast<float*>(ws + w.lse2);
   a.pooled = reinterpret_cast<float*>(ws + w.pooled);
-  KASCADE_TRY(launch_prefill_dense(a, s));
-  KASCADE_TRY(launch_prefill_pool(a, s));
-  KASCADE_TRY(launch_topk_prefill(a.pooled, p->batch, a.hkv, a.n, a.tile, p->top_k, idx, s));
+  KASCADE_TRY("prefill_dense", launch_prefill_dense(a, s));
+  KASCADE_TRY("prefill_pool", launch_prefill_pool(a, s));
+  KASCADE_TRY("topk_prefill", launch_topk_prefill(a.pooled, p->batch, a.hkv, a.n, a.tile, p->top_k, idx, s));
   if (lse)
-    KASCADE_TRY(launch_lse2_to_lse(a.lse2, lse, (size_t)p->batch * a.hq * a.n, s));
+    KASCADE_TRY("lse_convert", launch_lse2_to_lse(a.lse2, lse, (size_t)p->batch * a.hq * a.n, s));
   return KASCADE_OK;
 }
 
@@ -285,8 +335,45 @@ int kascade_reuse_prefill(const kascade_problem* p, const void* q, const void* k
   rc = check_workspace(p, KASCADE_OP_REUSE_PREFILL, workspace, workspace_bytes);
   if (rc) return rc;
   PrefillArgs a = prefill_args(p, q, k, v, idx, out);
-  KASCADE_TRY(launch_prefill_reuse(a, static_cast<hipStream_t>(stream)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  KASCADE_TRY("prefill_gather", launch_prefill_reuse(a, s));
   return KASCADE_OK;
+}
+
+int kascade_timing_enable(int on) {
+  Timing& t = timing();
+  std::lock_guard<std::mutex> lock(t.mu);
+  const int prev = t.on ? 1 : 0;
+  t.on = on != 0;
+  return prev;
+}
+
+int kascade_timing_collect(kascade_kernel_time* out, int max_entries) {
+  Timing& t = timing();
+  std::lock_guard<std::mutex> lock(t.mu);
+  int n = 0, rc = 0;
+  for (const TimedLaunch& l : t.pending) {
+    float ms = 0.f;
+    if (hipEventSynchronize(l.stop) != hipSuccess || hipEventElapsedTime(&ms, l.start, l.stop) != hipSuccess) {
+      rc = -1;
+    } else {
+      int i = 0;
+      while (i < n && strncmp(out[i].name, l.name, sizeof out[i].name) != 0) ++i;
+      if (i == n && n < max_entries) {
+        memset(&out[n], 0, sizeof out[n]);
+        strncpy(out[n].name, l.name, sizeof out[n].name - 1);
+        ++n;
+      }
+      if (i < n) {
+        out[i].total_ms += ms;
+        out[i].launches += 1;
+      }
+    }
+    t.spare.push_back(l.start);
+    t.spare.push_back(l.stop);
+  }
+  t.pending.clear();
+  return rc ? rc : n;
 }
 
 }  // extern "C"

@@ -17,7 +17,7 @@ OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 
 EXPORTS = ("kascade_validate", "kascade_workspace_bytes", "kascade_status_string",
            "kascade_anchor_decode", "kascade_reuse_decode", "kascade_anchor_prefill",
-           "kascade_reuse_prefill")
+           "kascade_reuse_prefill", "kascade_timing_enable", "kascade_timing_collect")
 
 
 class KascadeError(RuntimeError):
@@ -39,6 +39,11 @@ class Problem(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("dtype", ctypes.c_int32),
     ]
+
+
+class KernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 40), ("total_ms", ctypes.c_double),
+                ("launches", ctypes.c_int64)]
 
 
 class Library:
@@ -63,7 +68,23 @@ class Library:
             f = getattr(lib, name)
             f.argtypes = args
             f.restype = ctypes.c_int
+        lib.kascade_timing_enable.argtypes = [ctypes.c_int]
+        lib.kascade_timing_enable.restype = ctypes.c_int
+        lib.kascade_timing_collect.argtypes = [ctypes.POINTER(KernelTime), ctypes.c_int]
+        lib.kascade_timing_collect.restype = ctypes.c_int
         self.lib = lib
+
+    # -- per-kernel timing -----------------------------------------------------
+    def timing_enable(self, on=True):
+        return self.lib.kascade_timing_enable(1 if on else 0)
+
+    def timing_collect(self, max_entries=64):
+        """{kernel name: (total ms, launches)} since the last collect; waits for the events."""
+        buf = (KernelTime * max_entries)()
+        n = self.lib.kascade_timing_collect(buf, max_entries)
+        if n < 0:
+            raise KascadeError(ERR_HIP, "kascade_timing_collect failed")
+        return {buf[i].name.decode(): (buf[i].total_ms, buf[i].launches) for i in range(n)}
 
     # -- host-only queries ------------------------------------------------------
     def validate(self, prob, op):
