@@ -7,7 +7,10 @@ One step = one pass of the whole hot path over one batch of synthetic input:
   * causal prefill at 8K (B=1, Hq=32, Hkv=8, d=128, T=128, k=1024, bf16): one
     anchor layer (row log-sum-exp and dense output, pooled tile scores, per
     tile top-k) and three reuse layers.
-All inputs are resident in HBM before timing starts. Prints one JSON line.
+All inputs are resident in HBM before timing starts. The step is timed as HIP
+graph replays (the same kernels, without host launch gaps); an eager pass
+gives per-call times and, through the library's per-kernel HIP events, the
+per-kernel times behind the roofline. Prints one JSON line.
 
 value = decode attention microseconds per layer (mean of the four decode
 layers); the decode reuse-layer HBM rate and the prefill tokens/s sit beside it.
@@ -111,8 +114,12 @@ class PrefillStack:
         return total
 
 
+def _event():
+    return torch.cuda.Event(enable_timing=True)
+
+
 def _record():
-    e = torch.cuda.Event(enable_timing=True)
+    e = _event()
     e.record()
     return e
 
@@ -192,8 +199,39 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # timed region: K steps, per-call marks on the current stream, per-kernel
-    # events inside the library
+    # The step as two HIP graphs (decode stack, prefill stack): replays carry
+    # no host launch cost between the short kernels of a layer.
+    graphs = {}
+    for name, stack in (("decode", dec), ("prefill", pre)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            stack.run()
+        graphs[name] = g
+    for _ in range(args.warmup):
+        for g in graphs.values():
+            g.replay()
+    torch.cuda.synchronize()
+    start_g, stop_g = _event(), _event()
+    gt = {n: 0.0 for n in graphs}
+    start_g.record()
+    for _ in range(args.steps):
+        for g in graphs.values():
+            g.replay()
+    stop_g.record()
+    torch.cuda.synchronize()
+    total_ms = start_g.elapsed_time(stop_g)
+    # per-stack time from a second pass that times each graph on its own
+    for n, g in graphs.items():
+        a, b = _event(), _event()
+        a.record()
+        for _ in range(args.steps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        gt[n] = a.elapsed_time(b) / args.steps
+
+    # eager pass: per-call marks on the current stream and per-kernel events
+    # inside the library
     lib.timing_collect()
     lib.timing_enable(True)
     marks = []
@@ -205,7 +243,7 @@ def main():
     torch.cuda.synchronize()
     lib.timing_enable(False)
     kernels = lib.timing_collect()
-    total_ms = start.elapsed_time(stop)
+    eager_ms_per_step = start.elapsed_time(stop) / args.steps
     ms_per_step = total_ms / args.steps
 
     calls = {}
@@ -218,8 +256,8 @@ def main():
     kern = {n: (ms / cnt) for n, (ms, cnt) in kernels.items()}
 
     wd, wp = dec.w, pre.w
-    t_dec_layer_ms = (avg["decode_anchor"] + (wd.layers - 1) * avg["decode_reuse"]) / wd.layers
-    t_pre_stack_ms = avg["prefill_anchor"] + (wp.layers - 1) * avg["prefill_reuse"]
+    t_dec_layer_ms = gt["decode"] / wd.layers
+    t_pre_stack_ms = gt["prefill"]
     prefill_tps = wp.batch * wp.n * wp.layers / (t_pre_stack_ms * 1e-3)
     reuse_gbs = dec.reuse_bytes() / (kern["decode_attn_gather"] * 1e-3) / 1e9
     reuse_call_gbs = dec.reuse_bytes() / (avg["decode_reuse"] * 1e-3) / 1e9
@@ -265,6 +303,9 @@ def main():
         "roofline": roofline,
         "metrics": {
             "decode_us_per_layer": round(t_dec_layer_ms * 1e3, 3),
+            "decode_stack_us_graph": round(gt["decode"] * 1e3, 2),
+            "prefill_stack_us_graph": round(gt["prefill"] * 1e3, 2),
+            "eager_ms_per_step": round(eager_ms_per_step, 4),
             "decode_anchor_us": round(avg["decode_anchor"] * 1e3, 2),
             "decode_reuse_us": round(avg["decode_reuse"] * 1e3, 2),
             "decode_reuse_hbm_gbs_kernel": round(reuse_gbs, 1),

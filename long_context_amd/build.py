@@ -20,30 +20,33 @@ FLAGS = [
 ]
 
 
-def _compile(src):
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+def _compile(src, build_dir=BUILD, defines=()):
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
     return obj
 
 
-def build(verbose=False):
-    """Compile every kernel source for gfx950 and link the shared library."""
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose=False, library=LIBRARY, build_dir=BUILD, defines=()):
+    """Compile every kernel source for gfx950 and link the shared library.
+
+    `defines` (NAME=VALUE strings) and a different `library` path build a
+    variant of the library with other compile-time settings."""
+    os.makedirs(build_dir, exist_ok=True)
     sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(sources))) as ex:
-        objs = list(ex.map(_compile, sources))
-    tmp = LIBRARY + ".tmp"
+        objs = list(ex.map(lambda src: _compile(src, build_dir, defines), sources))
+    tmp = library + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIBRARY)
+    os.replace(tmp, library)
     if verbose:
-        print(LIBRARY)
-    return LIBRARY
+        print(library)
+    return library
 
 
 if __name__ == "__main__":

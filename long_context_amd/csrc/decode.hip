@@ -32,11 +32,30 @@ namespace {
 
 constexpr int kWavesPerBlock = 4;
 
+constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (log2 units)
+
+// Registers of one 32-key chunk in flight: K and V rows as A operands and the
+// validity of the chunk's 32 list entries (bit e = entry e usable).
+#ifndef KASCADE_DECODE_V_LATE
+#define KASCADE_DECODE_V_LATE 0
+#endif
+// V rows are requested after the scores of their chunk are computed, into the
+// registers K used, so that more wavefronts fit per SIMD.
+constexpr bool kVLate = KASCADE_DECODE_V_LATE != 0;
+
+template <int C>
+struct DecodeStage {
+  bf16x8 k[2][C];
+  bf16x8 v[2][kVLate ? 1 : C];
+  int row[2];
+  uint32_t valid;
+};
+
 template <int D, bool GATHER, bool WITH_PV, bool LOGITS>
 __global__ __launch_bounds__(256) void decode_attn_bf16(DecodeArgs a) {
   constexpr int C = D / 32;  // contraction chunks of 32 along d
   const int lane = threadIdx.x & 63;
-  const int split = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  const int split = blockIdx.x * kWavesPerBlock + wave_id();
   if (split >= a.splits) return;
   const int kvh = blockIdx.y, b = blockIdx.z;
   const int n = lane & 15;   // head column (B operand / C column) and A-operand row
@@ -65,91 +84,149 @@ __global__ __launch_bounds__(256) void decode_attn_bf16(DecodeArgs a) {
 
   const int begin = split * a.keys_per_split;
   const int end = min(begin + a.keys_per_split, a.list_len);
+  const int nchunk = (end - begin + 31) / 32;
+
+  // Gather mode: lane l reads list entry j0 + (l & 31); rows and validity of
+  // the chunk follow by lane exchange, so each entry is read once.
+  auto entry_key = [&](int j0) __attribute__((always_inline)) {
+    const int pos = j0 + (lane & 31);
+    int key = (GATHER && pos < end) ? list[pos] : -1;
+    return (unsigned)key < (unsigned)a.n ? key : -1;
+  };
+  auto load_stage = [&](DecodeStage<C>& st, int key_lane, int j0) __attribute__((always_inline)) {
+    int row[2];
+    if (GATHER) {
+      st.valid = (uint32_t)__ballot(key_lane >= 0);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int r = __shfl(key_lane, 16 * t + n);
+        row[t] = r < 0 ? 0 : r;  // unusable entries read row 0, masked below
+      }
+    } else {
+      const int left = end - j0;
+      st.valid = left >= 32 ? 0xffffffffu : ((1u << left) - 1u);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) row[t] = j0 + 16 * t + n < end ? j0 + 16 * t + n : 0;
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      st.row[t] = row[t];
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        st.k[t][c] = load_bf16x8(kb + (size_t)row[t] * D + 32 * c + 8 * qg);
+        if (WITH_PV && !kVLate) st.v[t][c] = load_bf16x8(vb + (size_t)row[t] * D + 32 * c + 8 * qg);
+      }
+    }
+  };
 
   float m = kNegBig, l = 0.0f;
   f32x4 acc[D / 16];
 #pragma unroll
   for (int i = 0; i < D / 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int j0 = begin; j0 < end; j0 += 32) {
-    // Row loaded by this lane for tiles t = 0, 1 (keys j0 + 16t + n).
-    int row[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int pos = j0 + 16 * t + n;
-      int key = pos < end ? (GATHER ? list[pos] : pos) : -1;
-      row[t] = (key < 0 || key >= a.n) ? 0 : key;  // masked keys read row 0, discarded
-    }
-    // Keys held in this lane's accumulator slots: j0 + 16t + 4qg + r.
-    bool valid[2][4];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int pos = j0 + 16 * t + 4 * qg + r;
-        valid[t][r] = pos < end && (!GATHER || (unsigned)list[pos] < (unsigned)a.n);
-      }
-
-    bf16x8 ka[2][C];
-    bf16x8 va[2][C];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int c = 0; c < C; ++c) {
-        ka[t][c] = load_bf16x8(kb + (size_t)row[t] * D + 32 * c + 8 * qg);
-        if (WITH_PV) va[t][c] = load_bf16x8(vb + (size_t)row[t] * D + 32 * c + 8 * qg);
-      }
-
+  auto compute = [&](DecodeStage<C>& st, int j0) __attribute__((always_inline)) {
     float x[2][4];
     float cmax = kNegBig;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < C; ++c) s = mfma16x16x32(ka[t][c], bq[c], s);
+      for (int c = 0; c < C; ++c) s = mfma16x16x32(st.k[t][c], bq[c], s);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        x[t][r] = valid[t][r] ? s[r] * a.scale_log2 : -INFINITY;
+        const bool ok = (st.valid >> (16 * t + 4 * qg + r)) & 1u;
+        x[t][r] = ok ? s[r] * a.scale_log2 : -INFINITY;
         cmax = fmaxf(cmax, x[t][r]);
       }
       if (LOGITS && n < G) {
         float* dst = a.logits + (size_t)(b * a.hq + h0 + n) * a.logits_ld + j0 + 16 * t + 4 * qg;
-        if (valid[t][3]) {
+        if ((st.valid >> (16 * t + 4 * qg + 3)) & 1u) {
           *reinterpret_cast<f32x4*>(dst) = f32x4{x[t][0], x[t][1], x[t][2], x[t][3]};
         } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            if (valid[t][r]) dst[r] = x[t][r];
+            if ((st.valid >> (16 * t + 4 * qg + r)) & 1u) dst[r] = x[t][r];
         }
       }
     }
     cmax = group4_max(cmax);
-    const float mnew = fmaxf(m, cmax);
-    const float alpha = fast_exp2(m - mnew);
-    m = mnew;
-    l *= alpha;
+    // Lazy rescaling: the reference maximum moves only when a head's maximum
+    // grows by more than 2^8, so probabilities stay below 256.
+    float alpha = 1.0f;
+    const bool rescale = __any(cmax > m + kRescaleLog2);
+    if (rescale) {
+      const float mnew = fmaxf(m, cmax);
+      alpha = fast_exp2(m - mnew);
+      m = mnew;
+    }
     f32x4 p[2];
+    float lsum = 0.f;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         p[t][r] = fast_exp2(x[t][r] - m);
-        l += p[t][r];
+        lsum += p[t][r];
       }
+    l = l * alpha + lsum;
     if (WITH_PV) {
       const bf16x8 pb = pack_bf16x8(p[0], p[1]);
+      if (rescale) {
 #pragma unroll
-      for (int i = 0; i < D / 16; ++i) acc[i] *= alpha;
+        for (int i = 0; i < D / 16; ++i) acc[i] *= alpha;
+      }
+      if (kVLate) {  // K's registers are free now
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int c = 0; c < C; ++c) st.k[t][c] = load_bf16x8(vb + (size_t)st.row[t] * D + 32 * c + 8 * qg);
+      }
 #pragma unroll
       for (int c = 0; c < C; ++c)
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-          f32x4 t0 = mfma16x16x32(va[0][c], sel[half], z);
-          f32x4 t1 = mfma16x16x32(va[1][c], sel[half], z);
+          const bf16x8 v0 = kVLate ? st.k[0][c] : st.v[0][kVLate ? 0 : c];
+          const bf16x8 v1 = kVLate ? st.k[1][c] : st.v[1][kVLate ? 0 : c];
+          const f32x4 t0 = mfma16x16x32(v0, sel[half], z);
+          const f32x4 t1 = mfma16x16x32(v1, sel[half], z);
           acc[2 * c + half] = mfma16x16x32(pack_bf16x8(t0, t1), pb, acc[2 * c + half]);
         }
     }
+  };
+
+  DecodeStage<C> s0, s1;
+#ifndef KASCADE_DECODE_PREFETCH
+#define KASCADE_DECODE_PREFETCH 1
+#endif
+  // Streaming the whole cache (dense) keeps the next chunk in flight; the
+  // short gathered lists run more wavefronts per SIMD instead.
+  if (GATHER || !KASCADE_DECODE_PREFETCH) {
+    for (int i = 0; i < nchunk; ++i) {
+      const int j0 = begin + 32 * i;
+      load_stage(s0, entry_key(j0), j0);
+      compute(s0, j0);
+    }
+  } else {
+  // Two chunks in flight: chunk i+1's rows are requested (and chunk i+2's
+  // list entries) before chunk i is computed.
+  int kn = entry_key(begin);
+  load_stage(s0, kn, begin);
+  kn = entry_key(begin + 32);
+  for (int i = 0; i < nchunk; i += 2) {
+    const int j0 = begin + 32 * i;
+    if (i + 1 < nchunk) {
+      load_stage(s1, kn, j0 + 32);
+      kn = entry_key(j0 + 64);
+    }
+    compute(s0, j0);
+    if (i + 1 >= nchunk) break;
+    if (i + 2 < nchunk) {
+      load_stage(s0, kn, j0 + 64);
+      kn = entry_key(j0 + 96);
+    }
+    compute(s1, j0 + 32);
+  }
   }
 
   l = group4_sum(l);
@@ -182,7 +259,7 @@ __global__ __launch_bounds__(256) void decode_attn_f32(DecodeArgs a) {
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
-  const int split = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  const int split = blockIdx.x * kWavesPerBlock + wave_id();
   if (split >= a.splits) return;
   const float* kb = static_cast<const float*>(a.k) + (size_t)(b * a.hkv + kvh) * a.n * D;
   const float* vb = static_cast<const float*>(a.v) + (size_t)(b * a.hkv + kvh) * a.n * D;
@@ -263,53 +340,44 @@ __global__ __launch_bounds__(256) void decode_attn_f32(DecodeArgs a) {
   }
 }
 
-// Merge per-split (max, sum, partial output) of one query row.
+// Merge per-split (max, sum, partial output) of query rows; one wave per row.
 template <bool BF16>
-__global__ __launch_bounds__(128) void decode_combine(const float* part_ml, const float* part_o,
-                                                     int splits, int d, void* out, float* lse) {
-  const int row = blockIdx.x;
+__global__ __launch_bounds__(256) void decode_combine(const float* part_ml, const float* part_o,
+                                                     int rows, int splits, int d, void* out,
+                                                     float* lse, float* lse2) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + wave_id();
+  if (row >= rows) return;
   const float* ml = part_ml + (size_t)row * splits * 2;
   float M = kNegBig;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, ml[2 * s]);
+  for (int s = lane; s < splits; s += 64) M = fmaxf(M, ml[2 * s]);
+  M = wave_max(M);
   float L = 0.f;
-  for (int s = 0; s < splits; ++s) L += ml[2 * s + 1] * fast_exp2(ml[2 * s] - M);
-  if (out) {
-    for (int c = threadIdx.x; c < d; c += blockDim.x) {
-      float o = 0.f;
-      for (int s = 0; s < splits; ++s)
-        o += part_o[((size_t)row * splits + s) * d + c] * fast_exp2(ml[2 * s] - M);
-      o = L > 0.f ? o / L : 0.f;
-      if (BF16)
-        static_cast<u16*>(out)[(size_t)row * d + c] = float_to_bf16_bits(o);
-      else
-        static_cast<float*>(out)[(size_t)row * d + c] = o;
+  for (int s = lane; s < splits; s += 64) L += ml[2 * s + 1] * fast_exp2(ml[2 * s] - M);
+  L = wave_sum(L);
+  if (lane == 0) {
+    if (lse) lse[row] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
+    if (lse2) lse2[row] = M + log2f(L);
+  }
+  if (!out) return;
+  const float inv = L > 0.f ? 1.0f / L : 0.f;
+  for (int c = lane; c < d; c += 64) {
+    float o = 0.f;
+    const float* po = part_o + (size_t)row * splits * d + c;
+    int s = 0;
+    for (; s + 4 <= splits; s += 4) {
+      const float w0 = fast_exp2(ml[2 * s] - M), w1 = fast_exp2(ml[2 * s + 2] - M);
+      const float w2 = fast_exp2(ml[2 * s + 4] - M), w3 = fast_exp2(ml[2 * s + 6] - M);
+      o += po[(size_t)s * d] * w0 + po[(size_t)(s + 1) * d] * w1 + po[(size_t)(s + 2) * d] * w2 +
+           po[(size_t)(s + 3) * d] * w3;
     }
+    for (; s < splits; ++s) o += po[(size_t)s * d] * fast_exp2(ml[2 * s] - M);
+    o *= inv;
+    if (BF16)
+      static_cast<u16*>(out)[(size_t)row * d + c] = float_to_bf16_bits(o);
+    else
+      static_cast<float*>(out)[(size_t)row * d + c] = o;
   }
-  if (lse && threadIdx.x == 0) lse[row] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
-}
-
-__global__ __launch_bounds__(256) void decode_pool(const float* logits, const float* part_ml,
-                                                   int hq, int hkv, int group, int n, int splits,
-                                                   float* pooled) {
-  const size_t ld = decode_logits_ld(n);
-  __shared__ float lse2[kMaxGroup];
-  const int kvh = blockIdx.y, b = blockIdx.z;
-  if (threadIdx.x < group) {
-    const float* ml = part_ml + (size_t)(b * hq + kvh * group + threadIdx.x) * splits * 2;
-    float M = kNegBig;
-    for (int s = 0; s < splits; ++s) M = fmaxf(M, ml[2 * s]);
-    float L = 0.f;
-    for (int s = 0; s < splits; ++s) L += ml[2 * s + 1] * fast_exp2(ml[2 * s] - M);
-    lse2[threadIdx.x] = M + log2f(L);
-  }
-  __syncthreads();
-  const int j = blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= n) return;
-  float acc = 0.f;
-  for (int g = 0; g < group; ++g)
-    acc += fast_exp2(logits[(size_t)(b * hq + kvh * group + g) * ld + j] - lse2[g]);
-  // The sum over heads ranks keys exactly as the mean does.
-  pooled[(size_t)(b * hkv + kvh) * n + j] = acc;
 }
 
 template <int D>
@@ -345,22 +413,15 @@ hipError_t launch_decode_attn(const DecodeArgs& a, bool bf16, bool gather, bool 
 }
 
 hipError_t launch_decode_combine(const float* part_ml, const float* part_o, int rows, int splits,
-                                 int d, bool bf16, void* out, float* lse, hipStream_t s) {
+                                 int d, bool bf16, void* out, float* lse, float* lse2,
+                                 hipStream_t s) {
+  const dim3 grid((rows + 3) / 4), block(256);
   if (bf16)
-    hipLaunchKernelGGL(decode_combine<true>, dim3(rows), dim3(128), 0, s, part_ml, part_o, splits,
-                       d, out, lse);
+    hipLaunchKernelGGL(decode_combine<true>, grid, block, 0, s, part_ml, part_o, rows, splits, d,
+                       out, lse, lse2);
   else
-    hipLaunchKernelGGL(decode_combine<false>, dim3(rows), dim3(128), 0, s, part_ml, part_o, splits,
-                       d, out, lse);
-  return hipGetLastError();
-}
-
-hipError_t launch_decode_pool(const float* logits, const float* part_ml, int batch, int hq,
-                              int hkv, int group, int n, int splits, float* pooled,
-                              hipStream_t s) {
-  dim3 grid((n + 255) / 256, hkv, batch);
-  hipLaunchKernelGGL(decode_pool, grid, dim3(256), 0, s, logits, part_ml, hq, hkv, group, n,
-                     splits, pooled);
+    hipLaunchKernelGGL(decode_combine<false>, grid, block, 0, s, part_ml, part_o, rows, splits, d,
+                       out, lse, lse2);
   return hipGetLastError();
 }
 

@@ -72,15 +72,38 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// The values of lanes l and l^16 (v_permlane16_swap) and of lanes l and l^32
+// (v_permlane32_swap): register-to-register lane exchanges on gfx950.
+__device__ __forceinline__ void pair16(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+  a = __int_as_float(r[0]);
+  b = __int_as_float(r[1]);
+}
+
+__device__ __forceinline__ void pair32(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+  a = __int_as_float(r[0]);
+  b = __int_as_float(r[1]);
+}
+
 // Reductions across the four lane groups (lanes l, l^16, l^32, l^48).
 __device__ __forceinline__ float group4_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  return fmaxf(v, __shfl_xor(v, 32));
+  float a, b;
+  pair16(v, a, b);
+  pair32(fmaxf(a, b), a, b);
+  return fmaxf(a, b);
 }
 
 __device__ __forceinline__ float group4_sum(float v) {
-  v += __shfl_xor(v, 16);
-  return v + __shfl_xor(v, 32);
+  float a, b;
+  pair16(v, a, b);
+  pair32(a + b, a, b);
+  return a + b;
+}
+
+// Wave index as a scalar, so that wave-level conditions become scalar branches.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 }
 
 }  // namespace kascade

@@ -15,7 +15,10 @@ namespace {
 using namespace kascade;
 
 constexpr size_t kAlign = 256;
-constexpr int kTargetWaves = 2048;  // about eight wavefronts per compute unit
+#ifndef KASCADE_TARGET_WAVES
+#define KASCADE_TARGET_WAVES 2048
+#endif
+constexpr int kTargetWaves = KASCADE_TARGET_WAVES;  // about eight wavefronts per compute unit
 constexpr int kMaxGroup = 16;       // query heads per KV head handled together
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -68,7 +71,7 @@ DecodeSplit decode_split(const kascade_problem* p, int len) {
 
 struct DecodeWorkspace {
   DecodeSplit split;
-  size_t part_ml, part_o, logits, pooled, total;  // byte offsets
+  size_t part_ml, part_o, logits, lse2, pooled, total;  // byte offsets
 };
 
 DecodeWorkspace decode_workspace(const kascade_problem* p, int op) {
@@ -84,6 +87,8 @@ DecodeWorkspace decode_workspace(const kascade_problem* p, int op) {
   if (anchor) {
     w.logits = off;
     off += align_up(rows * decode_logits_ld(p->kv_len) * sizeof(float));
+    w.lse2 = off;
+    off += align_up(rows * sizeof(float));
     w.pooled = off;
     off += align_up((size_t)p->batch * p->num_kv_heads * p->kv_len * sizeof(float));
   }
@@ -266,14 +271,13 @@ int kascade_anchor_decode(const kascade_problem* p, const void* q, const void* k
   a.list_len = p->kv_len;
   a.logits = reinterpret_cast<float*>(ws + w.logits);
   float* pooled = reinterpret_cast<float*>(ws + w.pooled);
+  float* lse2 = reinterpret_cast<float*>(ws + w.lse2);
   const bool bf16 = p->dtype == KASCADE_BF16;
   KASCADE_TRY("decode_attn_dense", launch_decode_attn(a, bf16, false, out != nullptr, s));
-  KASCADE_TRY("decode_pool", launch_decode_pool(a.logits, a.part_ml, p->batch, a.hq, a.hkv, a.group, a.n,
-                                 a.splits, pooled, s));
-  KASCADE_TRY("topk_decode", launch_topk_decode(pooled, p->batch * a.hkv, a.n, p->top_k, idx, s));
-  if (out || lse)
-    KASCADE_TRY("decode_combine", launch_decode_combine(a.part_ml, a.part_o, p->batch * a.hq,
-                                                        a.splits, a.d, bf16, out, lse, s));
+  KASCADE_TRY("decode_combine", launch_decode_combine(a.part_ml, a.part_o, p->batch * a.hq,
+                                                      a.splits, a.d, bf16, out, lse, lse2, s));
+  KASCADE_TRY("topk_decode", launch_topk_decode(a.logits, a.logits_ld, lse2, p->batch, a.hq, a.hkv,
+                                                a.group, a.n, p->top_k, pooled, idx, s));
   return KASCADE_OK;
 }
 
@@ -294,7 +298,7 @@ int kascade_reuse_decode(const kascade_problem* p, const void* q, const void* k,
   const bool bf16 = p->dtype == KASCADE_BF16;
   KASCADE_TRY("decode_attn_gather", launch_decode_attn(a, bf16, true, true, s));
   KASCADE_TRY("decode_combine", launch_decode_combine(a.part_ml, a.part_o, p->batch * a.hq,
-                                                      a.splits, a.d, bf16, out, nullptr, s));
+                                                      a.splits, a.d, bf16, out, nullptr, nullptr, s));
   return KASCADE_OK;
 }
 

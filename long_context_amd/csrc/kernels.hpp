@@ -31,21 +31,20 @@ __host__ __device__ inline int decode_logits_ld(int n) { return (n + 3) & ~3; }
 hipError_t launch_decode_attn(const DecodeArgs& a, bool bf16, bool gather, bool with_pv,
                               hipStream_t s);
 
-// Merge split partials into the output row and/or the log-sum-exp.
+// Merge split partials into the output rows, the natural-log lse and/or the
+// log2-domain lse2 (each optional).
 hipError_t launch_decode_combine(const float* part_ml, const float* part_o, int rows, int splits,
-                                 int d, bool bf16, void* out, float* lse, hipStream_t s);
-
-// pooled[b, kv, j] = sum over the group's heads of exp2(logit - lse2).
-hipError_t launch_decode_pool(const float* logits, const float* part_ml, int batch, int hq,
-                              int hkv, int group, int n, int splits, float* pooled,
-                              hipStream_t s);
+                                 int d, bool bf16, void* out, float* lse, float* lse2,
+                                 hipStream_t s);
 
 // ---- selection --------------------------------------------------------------
 
 // Exact top-k of non-negative float scores per segment, ascending indices,
 // lower index first among equal scores, -1 padding up to k.
-// Decode: segment s = (b, kv) covers scores[s*n .. s*n+n), writes idx[s*k ..].
-hipError_t launch_topk_decode(const float* scores, int segments, int n, int k, int32_t* idx,
+// Decode: segment (b, kv) is pooled here from the group's logits [., ld] and
+// lse2; above 32768 keys the scores go through `spill` [B*Hkv*n].
+hipError_t launch_topk_decode(const float* logits, int ld, const float* lse2, int batch, int hq,
+                              int hkv, int group, int n, int k, float* spill, int32_t* idx,
                               hipStream_t s);
 // Prefill: segment (b, kv, t) covers prefix_t = min((t+1)*T, N) scores stored
 // ragged: base (b*Hkv + kv) * ragged_len + T*t*(t+1)/2.

@@ -29,39 +29,55 @@ namespace kascade {
 
 namespace {
 
-constexpr int kKeyChunk = 64;
-constexpr int kRowsPerWave = 32;
-constexpr int kTile = 128;            // query tile; four waves of 32 rows
-constexpr int kLdsPad = 8;            // bf16 elements of padding per LDS row
+constexpr int kKeyChunk = 64;      // keys staged per pipeline step
+constexpr int kRowsPerWave = 32;   // query rows per wavefront in prefill_attn
+constexpr int kTile = 128;         // query tile: four wavefronts of 32 rows
+constexpr int kLdsPad = 16;        // bf16 elements of padding per LDS row
+constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (log2 units)
 
-__device__ __forceinline__ int pv_key(int qg, int s) {
-  // Contraction slot s of lane group qg in the P.V step, as laid out by the
-  // S^T accumulators of two consecutive 16-key tiles.
-  return s < 4 ? 4 * qg + s : 16 + 4 * qg + (s - 4);
+typedef __bf16 lds_bf16x4 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane L receives element
+// (L mod 4) of the 4-element vectors addressed by lanes 4s + L/4, s = 0..3.
+// Pointing lane L' at row (base + L'/4), columns (col + 4*(L' mod 4)) of a
+// row-major [row][col] tile therefore hands lane L the four values
+// tile[base + s][col + L], s = 0..3: a column of four rows, as the A operand
+// of a contraction over rows needs.
+__device__ __forceinline__ lds_bf16x4 lds_read_transposed(const __bf16* p) {
+  typedef __attribute__((address_space(3))) lds_bf16x4 lds_vec;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_vec*)(p));
 }
 
-template <int D, bool GATHER, bool WITH_O>
-__global__ __launch_bounds__(256) void prefill_attn(PrefillArgs a) {
+template <int D, bool GATHER, bool WITH_O, int NH>
+__global__ __launch_bounds__(256 * NH) void prefill_attn(PrefillArgs a) {
   constexpr int C = D / 32;
   constexpr int LD = D + kLdsPad;
-  __shared__ __attribute__((aligned(16))) __bf16 ks[kKeyChunk * LD];
-  __shared__ __attribute__((aligned(16))) __bf16 vs[kKeyChunk * LD];
-  __shared__ int keys_s[kKeyChunk];
+  constexpr int THREADS = 256 * NH;
+  constexpr int VPR = D / 8;                             // 16-byte vectors per row
+  constexpr int LPT = kKeyChunk * VPR / THREADS;         // vectors per thread per tensor
+  static_assert(LPT >= 1 && kKeyChunk * VPR % THREADS == 0, "chunk must split evenly");
+  __shared__ __attribute__((aligned(16))) __bf16 ks[2][kKeyChunk * LD];
+  __shared__ __attribute__((aligned(16))) __bf16 vs[WITH_O ? 2 : 1][WITH_O ? kKeyChunk * LD : 8];
+  __shared__ int keys_s[2][kKeyChunk];
+  __shared__ int info_s[2][4];  // gather mode: smallest valid key, largest key, any padding
 
   const int t = a.tiles - 1 - blockIdx.x;  // longest tiles first
-  const int h = blockIdx.y, b = blockIdx.z;
-  const int kvh = h / a.group;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int h = blockIdx.y * NH + wave / 4;
+  const int kvh = h / a.group;             // the NH heads of a block share one KV head
   const int n16 = lane & 15, qg = lane >> 4;
   const int prefix = min((t + 1) * kTile, a.n);
-  const int wrow0 = t * kTile + wave * kRowsPerWave;  // first row of this wave
+  const int wrow0 = t * kTile + (wave & 3) * kRowsPerWave;
+  const int wrow_last = min(wrow0 + kRowsPerWave, a.n) - 1;
+  const float sl2 = a.scale_log2;
 
   const u16* kb = a.k + (size_t)(b * a.hkv + kvh) * a.n * D;
   const u16* vb = a.v + (size_t)(b * a.hkv + kvh) * a.n * D;
   const int32_t* list = GATHER ? a.idx + ((size_t)(b * a.hkv + kvh) * a.tiles + t) * a.topk : nullptr;
   const int list_len = GATHER ? min(a.topk, prefix) : prefix;
+  const int nchunks = (list_len + kKeyChunk - 1) / kKeyChunk;
 
-  // Q^T operands for the wave's two 16-row blocks (rows past N read row N-1).
   bf16x8 bq[2][C];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
@@ -78,98 +94,158 @@ __global__ __launch_bounds__(256) void prefill_attn(PrefillArgs a) {
 #pragma unroll
     for (int i = 0; i < D / 16; ++i) acc[rb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  constexpr int kThreadsPerRow = D / 8;
-  constexpr int kRowsPerPass = 256 / kThreadsPerRow;
-
-  for (int j0 = 0; j0 < list_len; j0 += kKeyChunk) {
-    __syncthreads();  // previous chunk fully consumed
-    if (tid < kKeyChunk) {
-      const int pos = j0 + tid;
-      int key = pos < list_len ? (GATHER ? list[pos] : pos) : -1;
-      keys_s[tid] = key < a.n ? key : -1;  // entries outside the sequence are skipped
-    }
-    __syncthreads();
+  // ---- staging: chunk c's rows go global -> registers -> LDS ----------------
+  bf16x8 kr[LPT], vr[LPT];
+  int key_reg = -1;
+  auto key_at = [&](int pos) __attribute__((always_inline)) {
+    int key = pos < list_len ? (GATHER ? list[pos] : pos) : -1;
+    return key < a.n ? key : -1;  // entries outside the sequence are skipped
+  };
+  auto fetch = [&](int c) __attribute__((always_inline)) {
 #pragma unroll
-    for (int p = 0; p < kKeyChunk / kRowsPerPass; ++p) {
-      const int rr = p * kRowsPerPass + tid / kThreadsPerRow;
-      const int cc = (tid % kThreadsPerRow) * 8;
-      const int key = keys_s[rr];
-      const int src = key < 0 ? 0 : key;
-      *reinterpret_cast<bf16x8*>(&ks[rr * LD + cc]) = load_bf16x8(kb + (size_t)src * D + cc);
-      if (WITH_O)
-        *reinterpret_cast<bf16x8*>(&vs[rr * LD + cc]) = load_bf16x8(vb + (size_t)src * D + cc);
+    for (int i = 0; i < LPT; ++i) {
+      const int slot = tid + i * THREADS;
+      const int row = slot / VPR, col = (slot % VPR) * 8;
+      const int key = key_at(c * kKeyChunk + row);
+      const size_t src = (size_t)(key < 0 ? 0 : key) * D + col;
+      kr[i] = load_bf16x8(kb + src);
+      if (WITH_O) vr[i] = load_bf16x8(vb + src);
     }
-    __syncthreads();
-
-    // Smallest key of the chunk above every row of this wave: nothing to do.
-    int kmin = 0x7fffffff;
-    {
-      const int key = keys_s[lane];
-      if (key >= 0) kmin = key;
+    if (GATHER && tid < kKeyChunk) key_reg = key_at(c * kKeyChunk + tid);
+  };
+  auto stash = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) kmin = min(kmin, __shfl_xor(kmin, o));
+    for (int i = 0; i < LPT; ++i) {
+      const int slot = tid + i * THREADS;
+      const int row = slot / VPR, col = (slot % VPR) * 8;
+      *reinterpret_cast<bf16x8*>(&ks[buf][row * LD + col]) = kr[i];
+      if (WITH_O) *reinterpret_cast<bf16x8*>(&vs[buf][row * LD + col]) = vr[i];
     }
-    if (kmin > wrow0 + kRowsPerWave - 1) continue;
-
+    if (GATHER && wave == 0) {  // wave 0 holds the chunk's 64 keys, one per lane
+      keys_s[buf][lane] = key_reg;
+      int lo = key_reg >= 0 ? key_reg : 0x7fffffff, hi = key_reg;
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {  // two 32-key halves of the chunk
-      int kkey[2][4];
+      for (int o = 32; o > 0; o >>= 1) {
+        lo = min(lo, __shfl_xor(lo, o));
+        hi = max(hi, __shfl_xor(hi, o));
+      }
+      const bool pad = __any(key_reg < 0);
+      if (lane == 0) {
+        info_s[buf][0] = lo;
+        info_s[buf][1] = hi;
+        info_s[buf][2] = pad;
+      }
+    }
+  };
+
+  // ---- one 32-key half of a staged chunk -------------------------------------
+  auto half_step = [&](int buf, int c, int sub, bool masked) __attribute__((always_inline)) {
+    f32x4 s[2][2];  // [row block][key tile]; scores, then probabilities in place
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const __bf16* krow = &ks[buf][(32 * sub + 16 * kt + n16) * LD + 8 * qg];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) s[rb][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int cc = 0; cc < C; ++cc) {
+        const bf16x8 ak = *reinterpret_cast<const bf16x8*>(krow + 32 * cc);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) s[rb][kt] = mfma16x16x32(ak, bq[rb][cc], s[rb][kt]);
+      }
+    }
+    if (masked) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) kkey[kt][r] = keys_s[32 * sub + 16 * kt + 4 * qg + r];
-
-      f32x4 p[2][2];  // [row block][key tile]
-      float alpha[2];
+        for (int r = 0; r < 4; ++r) {
+          const int pos = c * kKeyChunk + 32 * sub + 16 * kt + 4 * qg + r;
+          const int key = GATHER ? keys_s[buf][pos - c * kKeyChunk] : (pos < list_len ? pos : -1);
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const int row = wrow0 + 16 * rb + n16;
-        float x[2][4], cmax = kNegBig;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          f32x4 s = {0.f, 0.f, 0.f, 0.f};
-          const __bf16* krow = &ks[(32 * sub + 16 * kt + n16) * LD];
-#pragma unroll
-          for (int c = 0; c < C; ++c)
-            s = mfma16x16x32(*reinterpret_cast<const bf16x8*>(krow + 32 * c + 8 * qg), bq[rb][c], s);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int key = kkey[kt][r];
-            x[kt][r] = (key >= 0 && key <= row) ? s[r] * a.scale_log2 : -INFINITY;
-            cmax = fmaxf(cmax, x[kt][r]);
-          }
+          for (int rb = 0; rb < 2; ++rb)
+            if (key < 0 || key > wrow0 + 16 * rb + n16) s[rb][kt][r] = -INFINITY;
         }
-        cmax = group4_max(cmax);
+    }
+    float alpha[2];
+    bool rescale[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      float cmax = fmaxf(fmaxf(fmaxf(s[rb][0][0], s[rb][0][1]), fmaxf(s[rb][0][2], s[rb][0][3])),
+                         fmaxf(fmaxf(s[rb][1][0], s[rb][1][1]), fmaxf(s[rb][1][2], s[rb][1][3])));
+      cmax = group4_max(cmax) * sl2;
+      // Lazy rescaling: keep the reference maximum unless some row's maximum
+      // grew by more than 2^8; probabilities then stay below 256 in fp32.
+      alpha[rb] = 1.0f;
+      rescale[rb] = __any(cmax > m[rb] + kRescaleLog2);
+      if (rescale[rb]) {
         const float mnew = fmaxf(m[rb], cmax);
         alpha[rb] = fast_exp2(m[rb] - mnew);
         m[rb] = mnew;
-        l[rb] *= alpha[rb];
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            p[rb][kt][r] = fast_exp2(x[kt][r] - mnew);
-            l[rb] += p[rb][kt][r];
-          }
       }
-      if (WITH_O) {
-        bf16x8 pb[2];
+      const float neg_m = -m[rb];
+      float lsum = 0.f;
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          pb[rb] = pack_bf16x8(p[rb][0], p[rb][1]);
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          s[rb][kt][r] = fast_exp2(fmaf(s[rb][kt][r], sl2, neg_m));
+          lsum += s[rb][kt][r];
+        }
+      l[rb] = l[rb] * alpha[rb] + lsum;
+    }
+    if (WITH_O) {
+      bf16x8 pb[2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        pb[rb] = pack_bf16x8(s[rb][0], s[rb][1]);
+        if (rescale[rb]) {
 #pragma unroll
           for (int i = 0; i < D / 16; ++i) acc[rb][i] *= alpha[rb];
         }
+      }
+      // V^T operand: lane (d = n16, group qg) needs keys 4qg..4qg+3 and
+      // 16+4qg..16+4qg+3 of the half, the order of the P^T accumulators.
+      const __bf16* v0 = &vs[WITH_O ? buf : 0][(32 * sub + 4 * qg + (n16 >> 2)) * LD + 4 * (n16 & 3)];
 #pragma unroll
-        for (int db = 0; db < D / 16; ++db) {
-          bf16x8 av;
+      for (int db = 0; db < D / 16; ++db) {
+        const lds_bf16x4 lo = lds_read_transposed(v0 + 16 * db);
+        const lds_bf16x4 hi = lds_read_transposed(v0 + 16 * LD + 16 * db);
+        const bf16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-          for (int s = 0; s < 8; ++s) av[s] = vs[(32 * sub + pv_key(qg, s)) * LD + 16 * db + n16];
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb) acc[rb][db] = mfma16x16x32(av, pb[rb], acc[rb][db]);
-        }
+        for (int rb = 0; rb < 2; ++rb) acc[rb][db] = mfma16x16x32(av, pb[rb], acc[rb][db]);
       }
     }
+  };
+  auto chunk_step = [&](int buf, int c, bool masked) __attribute__((always_inline)) {
+#pragma unroll 1
+    for (int sub = 0; sub < 2; ++sub) half_step(buf, c, sub, masked);
+  };
+
+  if (nchunks > 0) {
+    fetch(0);
+    stash(0);
+  }
+  __syncthreads();
+  if (nchunks > 1) fetch(1);
+  for (int c = 0; c < nchunks; ++c) {
+    const int buf = c & 1;
+    if (wrow0 < a.n) {
+      int vmin, vmax;
+      bool pad;
+      if (GATHER) {
+        vmin = info_s[buf][0];
+        vmax = info_s[buf][1];
+        pad = info_s[buf][2] != 0;
+      } else {
+        vmin = c * kKeyChunk;
+        vmax = min(vmin + kKeyChunk, list_len) - 1;
+        pad = vmin + kKeyChunk > list_len;
+      }
+      if (vmin <= wrow_last)  // otherwise every key is above every row of the wave
+        chunk_step(buf, c, pad || vmax > wrow0);
+    }
+    if (c + 1 < nchunks) stash(buf ^ 1);  // that buffer was released at the last barrier
+    __syncthreads();
+    if (c + 2 < nchunks) fetch(c + 2);
   }
 
 #pragma unroll
@@ -193,27 +269,39 @@ __global__ __launch_bounds__(256) void prefill_attn(PrefillArgs a) {
   }
 }
 
+// ---- anchor pass 2: pooled post-softmax probabilities per query tile ---------
+
+constexpr int kPoolWaves = 4;
 constexpr int kPoolKeysPerWave = 64;
-constexpr int kPoolKeysPerBlock = 4 * kPoolKeysPerWave;
+constexpr int kPoolKeys = kPoolWaves * kPoolKeysPerWave;  // keys per workgroup
+constexpr int kPoolRows = 64;                             // query rows per pipeline step
 
 template <int D>
-__global__ __launch_bounds__(256) void prefill_pool(PrefillArgs a) {
+__global__ __launch_bounds__(64 * kPoolWaves) void prefill_pool(PrefillArgs a) {
   constexpr int C = D / 32;
   constexpr int LD = D + kLdsPad;
-  __shared__ __attribute__((aligned(16))) __bf16 qs[16 * LD];
-  __shared__ float lse_s[16];
+  constexpr int THREADS = 64 * kPoolWaves;
+  constexpr int VPR = D / 8;
+  constexpr int LPT = kPoolRows * VPR / THREADS;
+  static_assert(LPT >= 1 && kPoolRows * VPR % THREADS == 0, "row block must split evenly");
+  __shared__ __attribute__((aligned(16))) __bf16 qs[2][kPoolRows * LD];
+  __shared__ __attribute__((aligned(16))) float ls[2][kPoolRows];
 
-  const int chunk = blockIdx.x, t = blockIdx.y;
+  // Tiles vary fastest across workgroups, so with a multiple of 8 tiles all key
+  // chunks of one tile (which stream the same query rows) share an XCD's L2.
+  const int t = blockIdx.x, chunk = blockIdx.y;
   const int kvh = blockIdx.z % a.hkv, b = blockIdx.z / a.hkv;
   const int prefix = min((t + 1) * kTile, a.n);
-  const int kbase = chunk * kPoolKeysPerBlock;
+  const int kbase = chunk * kPoolKeys;
   if (kbase >= prefix) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int n16 = lane & 15, qg = lane >> 4;
-  const int row0 = t * kTile, rows = prefix - row0;
+  const int row0 = t * kTile, nrows = prefix - row0;
   const int wkey0 = kbase + wave * kPoolKeysPerWave;
+  const float sl2 = a.scale_log2;
 
-  // K^T operands of this wave's 64 keys (keys past prefix read key 0, masked).
+  // K^T operands of this wave's 64 keys (keys past the prefix read row 0 and
+  // are never written out).
   const u16* kb = a.k + (size_t)(b * a.hkv + kvh) * a.n * D;
   bf16x8 bk[4][C];
 #pragma unroll
@@ -225,48 +313,87 @@ __global__ __launch_bounds__(256) void prefill_pool(PrefillArgs a) {
   }
   float colsum[4] = {0.f, 0.f, 0.f, 0.f};
 
-  const int blocks_per_head = (rows + 15) / 16;
-  for (int g = 0; g < a.group; ++g) {
-    const int h = kvh * a.group + g;
-    for (int rbk = 0; rbk < blocks_per_head; ++rbk) {
-      const int r0 = row0 + 16 * rbk;
-      if (r0 + 15 < kbase) continue;  // every key of the block is above every row
-      __syncthreads();
-      {
-        const int rr = tid / (D / 8), cc = (tid % (D / 8)) * 8;
-        if (rr < 16) {
-          const int row = min(r0 + rr, a.n - 1);
-          *reinterpret_cast<bf16x8*>(&qs[rr * LD + cc]) =
-              load_bf16x8(a.q + ((size_t)(b * a.hq + h) * a.n + row) * D + cc);
-        }
-        if (tid < 16) {
-          const int row = r0 + tid;
-          lse_s[tid] = row < a.n ? a.lse2[(size_t)(b * a.hq + h) * a.n + row] : INFINITY;
-        }
-      }
-      __syncthreads();
-      if (r0 + 15 < wkey0) continue;
-      bf16x8 aq[C];
+  // Steps: (head g of the group, 64-row block of the tile). Row blocks wholly
+  // below the workgroup's first key contribute nothing and are skipped.
+  const int nblk = (nrows + kPoolRows - 1) / kPoolRows;
+  int blk0 = 0;
+  while (blk0 < nblk && row0 + kPoolRows * (blk0 + 1) - 1 < kbase) ++blk0;
+  const int per_head = nblk - blk0;
+  const int nsteps = a.group * per_head;
+
+  bf16x8 qr[LPT];
+  float lr = INFINITY;
+  auto step_rows = [&](int s, int& h, int& r0) __attribute__((always_inline)) {
+    h = kvh * a.group + s / per_head;
+    r0 = row0 + kPoolRows * (blk0 + s % per_head);
+  };
+  auto fetch = [&](int s) __attribute__((always_inline)) {
+    int h, r0;
+    step_rows(s, h, r0);
+    const u16* qh = a.q + (size_t)(b * a.hq + h) * a.n * D;
 #pragma unroll
-      for (int c = 0; c < C; ++c)
-        aq[c] = *reinterpret_cast<const bf16x8*>(&qs[n16 * LD + 32 * c + 8 * qg]);
-      float lse_r[4];
+    for (int i = 0; i < LPT; ++i) {
+      const int slot = tid + i * THREADS;
+      const int row = slot / VPR, col = (slot % VPR) * 8;
+      qr[i] = load_bf16x8(qh + (size_t)min(r0 + row, a.n - 1) * D + col);
+    }
+    if (tid < kPoolRows) {
+      const int row = r0 + tid;
+      // Rows past N get +inf so that every probability they add is 0.
+      lr = row < a.n ? a.lse2[(size_t)(b * a.hq + h) * a.n + row] : INFINITY;
+    }
+  };
+  auto stash = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) lse_r[r] = lse_s[4 * qg + r];
+    for (int i = 0; i < LPT; ++i) {
+      const int slot = tid + i * THREADS;
+      const int row = slot / VPR, col = (slot % VPR) * 8;
+      *reinterpret_cast<bf16x8*>(&qs[buf][row * LD + col]) = qr[i];
+    }
+    if (tid < kPoolRows) ls[buf][tid] = lr;
+  };
+  auto block_step = [&](int buf, int rr0, int rb, bool masked) __attribute__((always_inline)) {
+    bf16x8 aq[C];
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < C; ++c)
+      aq[c] = *reinterpret_cast<const bf16x8*>(&qs[buf][(16 * rb + n16) * LD + 32 * c + 8 * qg]);
+    const f32x4 lse = *reinterpret_cast<const f32x4*>(&ls[buf][16 * rb + 4 * qg]);
 #pragma unroll
-        for (int c = 0; c < C; ++c) s = mfma16x16x32(aq[c], bk[kt][c], s);
-        const int key = wkey0 + 16 * kt + n16;
+    for (int kt = 0; kt < 4; ++kt) {
+      f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = r0 + 4 * qg + r;
-          const float pr = fast_exp2(s[r] * a.scale_log2 - lse_r[r]);
-          colsum[kt] += (key <= row && row < a.n) ? pr : 0.f;
-        }
+      for (int c = 0; c < C; ++c) s = mfma16x16x32(aq[c], bk[kt][c], s);
+      const int key = wkey0 + 16 * kt + n16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float pr = fast_exp2(fmaf(s[r], sl2, -lse[r]));
+        colsum[kt] += (!masked || key <= rr0 + 4 * qg + r) ? pr : 0.f;
       }
     }
+  };
+
+  if (nsteps > 0) {
+    fetch(0);
+    stash(0);
+  }
+  __syncthreads();
+  if (nsteps > 1) fetch(1);
+  for (int s = 0; s < nsteps; ++s) {
+    const int buf = s & 1;
+    int h, r0;
+    step_rows(s, h, r0);
+#pragma unroll
+    for (int rb = 0; rb < kPoolRows / 16; ++rb) {
+      const int rr0 = r0 + 16 * rb;
+      if (rr0 + 15 < wkey0 || rr0 >= prefix) continue;  // no key of the wave is visible
+      if (wkey0 + kPoolKeysPerWave - 1 > rr0)
+        block_step(buf, rr0, rb, true);
+      else
+        block_step(buf, rr0, rb, false);
+    }
+    if (s + 1 < nsteps) stash(buf ^ 1);
+    __syncthreads();
+    if (s + 2 < nsteps) fetch(s + 2);
   }
 
   const size_t ragged = prefill_ragged_len(a.n, kTile);
@@ -286,33 +413,36 @@ __global__ void lse2_to_lse_kernel(const float* lse2, float* lse, size_t count) 
 
 }  // namespace
 
-hipError_t launch_prefill_dense(const PrefillArgs& a, hipStream_t s) {
-  dim3 grid(a.tiles, a.hq, a.batch), block(256);
-  const bool with_o = a.out != nullptr;
-  if (a.d == 128) {
-    if (with_o) hipLaunchKernelGGL((prefill_attn<128, false, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((prefill_attn<128, false, false>), grid, block, 0, s, a);
-  } else if (a.d == 64) {
-    if (with_o) hipLaunchKernelGGL((prefill_attn<64, false, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((prefill_attn<64, false, false>), grid, block, 0, s, a);
+template <int D, bool GATHER, bool WITH_O>
+hipError_t launch_attn(const PrefillArgs& a, hipStream_t s) {
+  // Two heads of a GQA group per workgroup share every staged K/V chunk.
+  if (a.group % 2 == 0) {
+    dim3 grid(a.tiles, a.hq / 2, a.batch);
+    hipLaunchKernelGGL((prefill_attn<D, GATHER, WITH_O, 2>), grid, dim3(512), 0, s, a);
   } else {
-    return hipErrorInvalidValue;
+    dim3 grid(a.tiles, a.hq, a.batch);
+    hipLaunchKernelGGL((prefill_attn<D, GATHER, WITH_O, 1>), grid, dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }
 
+hipError_t launch_prefill_dense(const PrefillArgs& a, hipStream_t s) {
+  const bool with_o = a.out != nullptr;
+  if (a.d == 128) return with_o ? launch_attn<128, false, true>(a, s) : launch_attn<128, false, false>(a, s);
+  if (a.d == 64) return with_o ? launch_attn<64, false, true>(a, s) : launch_attn<64, false, false>(a, s);
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_prefill_reuse(const PrefillArgs& a, hipStream_t s) {
-  dim3 grid(a.tiles, a.hq, a.batch), block(256);
-  if (a.d == 128) hipLaunchKernelGGL((prefill_attn<128, true, true>), grid, block, 0, s, a);
-  else if (a.d == 64) hipLaunchKernelGGL((prefill_attn<64, true, true>), grid, block, 0, s, a);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
+  if (a.d == 128) return launch_attn<128, true, true>(a, s);
+  if (a.d == 64) return launch_attn<64, true, true>(a, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_prefill_pool(const PrefillArgs& a, hipStream_t s) {
-  dim3 grid((a.n + kPoolKeysPerBlock - 1) / kPoolKeysPerBlock, a.tiles, a.hkv * a.batch);
-  if (a.d == 128) hipLaunchKernelGGL(prefill_pool<128>, grid, dim3(256), 0, s, a);
-  else if (a.d == 64) hipLaunchKernelGGL(prefill_pool<64>, grid, dim3(256), 0, s, a);
+  dim3 grid(a.tiles, (a.n + kPoolKeys - 1) / kPoolKeys, a.hkv * a.batch);
+  if (a.d == 128) hipLaunchKernelGGL(prefill_pool<128>, grid, dim3(64 * kPoolWaves), 0, s, a);
+  else if (a.d == 64) hipLaunchKernelGGL(prefill_pool<64>, grid, dim3(64 * kPoolWaves), 0, s, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -166,3 +166,45 @@ def test_decode_128k_sampled(lib, orc):
     w = synth.WORKLOADS["decode_128k"]
     log("[decode] case=decode_128k full size, sampled units")
     _sampled_full(orc, w, [(0, 0), (1, 5), (3, 7)], seed=22)
+
+
+def test_graph_replay_matches_eager(lib):
+    """Decode and prefill anchor + reuse captured in a HIP graph: every replay,
+    with eager work and synchronisations between replays, reproduces the eager
+    results bit for bit."""
+    log("[graph] case=replay_matches_eager")
+    wd = _small("graph_dec", wid=912)
+    (q0, k0, v0), (q1, k1, v1) = [tuple(t.to(DEV) for t in layer) for layer in _layers(wd)]
+    wp = synth.Workload("graph_pre", 913, "prefill", 1, 8, 2, 128, 700, 192, 128, "bf16", 2, 8, 1.0, 4)
+    (p0, pk0, pv0), (p1, pk1, pv1) = [tuple(t.to(DEV) for t in layer) for layer in synth.make_stack(wp, "cpu")]
+    outs = {n: torch.empty_like(t) for n, t in (("da", q0), ("dr", q1), ("pa", p0), ("pr", p1))}
+    didx = torch.empty((wd.batch, wd.hkv, 1, wd.k), dtype=torch.int32, device=DEV)
+    pidx = torch.empty((1, wp.hkv, wp.tiles, wp.k), dtype=torch.int32, device=DEV)
+    ws = {
+        "ad": K.workspace(K.problem(q0, k0, wd.k, 1), K.OP_ANCHOR_DECODE, DEV),
+        "rd": K.workspace(K.problem(q1, k1, wd.k, 1), K.OP_REUSE_DECODE, DEV),
+        "ap": K.workspace(K.problem(p0, pk0, wp.k, wp.tile), K.OP_ANCHOR_PREFILL, DEV),
+    }
+
+    def run():
+        K.anchor_decode(q0, k0, v0, wd.k, out=outs["da"], idx=didx, ws=ws["ad"])
+        K.reuse_decode(q1, k1, v1, didx, out=outs["dr"], ws=ws["rd"])
+        K.anchor_prefill(p0, pk0, pv0, wp.k, wp.tile, out=outs["pa"], idx=pidx, ws=ws["ap"])
+        K.reuse_prefill(p1, pk1, pv1, pidx, wp.tile, out=outs["pr"])
+
+    run()
+    torch.cuda.synchronize()
+    ref = {n: t.clone() for n, t in outs.items()}
+    ref_idx = (didx.clone(), pidx.clone())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for _ in range(3):
+        for t in list(outs.values()) + [didx, pidx]:
+            t.zero_()                       # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for n in outs:
+            assert torch.equal(outs[n], ref[n]), n
+        assert torch.equal(didx, ref_idx[0]) and torch.equal(pidx, ref_idx[1])
