@@ -16,6 +16,9 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
     # Packed fp32 instructions stay off: the compiler keeps to scalar fp32 ops.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Matrix-core results in ordinary VGPRs, so the vector ALU reads them
+    # without a copy out of the accumulation registers.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 

@@ -276,6 +276,11 @@ constexpr int kPoolKeysPerWave = 64;
 constexpr int kPoolKeys = kPoolWaves * kPoolKeysPerWave;  // keys per workgroup
 constexpr int kPoolRows = 64;                             // query rows per pipeline step
 
+#ifndef KASCADE_POOL_TILES
+#define KASCADE_POOL_TILES 1
+#endif
+constexpr int kPoolTiles = KASCADE_POOL_TILES;  // query tiles walked by one workgroup
+
 template <int D>
 __global__ __launch_bounds__(64 * kPoolWaves) void prefill_pool(PrefillArgs a) {
   constexpr int C = D / 32;
@@ -283,53 +288,56 @@ __global__ __launch_bounds__(64 * kPoolWaves) void prefill_pool(PrefillArgs a) {
   constexpr int THREADS = 64 * kPoolWaves;
   constexpr int VPR = D / 8;
   constexpr int LPT = kPoolRows * VPR / THREADS;
+  constexpr int kBlocksPerTile = kTile / kPoolRows;
   static_assert(LPT >= 1 && kPoolRows * VPR % THREADS == 0, "row block must split evenly");
   __shared__ __attribute__((aligned(16))) __bf16 qs[2][kPoolRows * LD];
   __shared__ __attribute__((aligned(16))) float ls[2][kPoolRows];
 
-  // Tiles vary fastest across workgroups, so with a multiple of 8 tiles all key
-  // chunks of one tile (which stream the same query rows) share an XCD's L2.
-  const int t = blockIdx.x, chunk = blockIdx.y;
+  // Workgroup = (segment of kPoolTiles query tiles, chunk of kPoolKeys keys,
+  // b, KV head). Its keys stay resident while it walks the tiles of the segment
+  // that have them as candidates. Segments vary fastest, so with a multiple of
+  // 8 segments all key chunks of one segment share an XCD's L2.
+  const int seg = blockIdx.x, chunk = blockIdx.y;
   const int kvh = blockIdx.z % a.hkv, b = blockIdx.z / a.hkv;
-  const int prefix = min((t + 1) * kTile, a.n);
   const int kbase = chunk * kPoolKeys;
-  if (kbase >= prefix) return;
+  const int t_first = max(seg * kPoolTiles, kbase / kTile);  // first tile whose prefix passes kbase
+  const int t_end = min((seg + 1) * kPoolTiles, a.tiles);
+  if (t_first >= t_end || kbase >= a.n) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int n16 = lane & 15, qg = lane >> 4;
-  const int row0 = t * kTile, nrows = prefix - row0;
   const int wkey0 = kbase + wave * kPoolKeysPerWave;
   const float sl2 = a.scale_log2;
+  const size_t ragged = prefill_ragged_len(a.n, kTile);
+  float* pooled_row = a.pooled + (size_t)(b * a.hkv + kvh) * ragged;
 
-  // K^T operands of this wave's 64 keys (keys past the prefix read row 0 and
-  // are never written out).
+  // K^T operands of this wave's 64 keys (keys past N read row 0 and are never
+  // written out).
   const u16* kb = a.k + (size_t)(b * a.hkv + kvh) * a.n * D;
   bf16x8 bk[4][C];
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) {
     const int key = wkey0 + 16 * kt + n16;
-    const u16* krow = kb + (size_t)(key < prefix ? key : 0) * D;
+    const u16* krow = kb + (size_t)(key < a.n ? key : 0) * D;
 #pragma unroll
     for (int c = 0; c < C; ++c) bk[kt][c] = load_bf16x8(krow + 32 * c + 8 * qg);
   }
   float colsum[4] = {0.f, 0.f, 0.f, 0.f};
 
-  // Steps: (head g of the group, 64-row block of the tile). Row blocks wholly
-  // below the workgroup's first key contribute nothing and are skipped.
-  const int nblk = (nrows + kPoolRows - 1) / kPoolRows;
-  int blk0 = 0;
-  while (blk0 < nblk && row0 + kPoolRows * (blk0 + 1) - 1 < kbase) ++blk0;
-  const int per_head = nblk - blk0;
-  const int nsteps = a.group * per_head;
+  // Steps: (tile, head of the group, 64-row block of the tile).
+  const int per_tile = a.group * kBlocksPerTile;
+  const int nsteps = (t_end - t_first) * per_tile;
 
   bf16x8 qr[LPT];
   float lr = INFINITY;
-  auto step_rows = [&](int s, int& h, int& r0) __attribute__((always_inline)) {
-    h = kvh * a.group + s / per_head;
-    r0 = row0 + kPoolRows * (blk0 + s % per_head);
+  auto step_rows = [&](int s, int& t, int& h, int& r0) __attribute__((always_inline)) {
+    t = t_first + s / per_tile;
+    const int w = s % per_tile;
+    h = kvh * a.group + w / kBlocksPerTile;
+    r0 = t * kTile + kPoolRows * (w % kBlocksPerTile);
   };
   auto fetch = [&](int s) __attribute__((always_inline)) {
-    int h, r0;
-    step_rows(s, h, r0);
+    int t, h, r0;
+    step_rows(s, t, h, r0);
     const u16* qh = a.q + (size_t)(b * a.hq + h) * a.n * D;
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
@@ -372,37 +380,41 @@ __global__ __launch_bounds__(64 * kPoolWaves) void prefill_pool(PrefillArgs a) {
     }
   };
 
-  if (nsteps > 0) {
-    fetch(0);
-    stash(0);
-  }
+  fetch(0);
+  stash(0);
   __syncthreads();
   if (nsteps > 1) fetch(1);
   for (int s = 0; s < nsteps; ++s) {
     const int buf = s & 1;
-    int h, r0;
-    step_rows(s, h, r0);
+    int t, h, r0;
+    step_rows(s, t, h, r0);
+    const int prefix = min((t + 1) * kTile, a.n);
+    if (wkey0 + kPoolKeysPerWave - 1 <= r0 && r0 + kPoolRows <= prefix) {
+      // Every key of the wave is visible to every row of the step: one
+      // straight-line body, so operand reads of a block overlap the previous one.
 #pragma unroll
-    for (int rb = 0; rb < kPoolRows / 16; ++rb) {
-      const int rr0 = r0 + 16 * rb;
-      if (rr0 + 15 < wkey0 || rr0 >= prefix) continue;  // no key of the wave is visible
-      if (wkey0 + kPoolKeysPerWave - 1 > rr0)
-        block_step(buf, rr0, rb, true);
-      else
-        block_step(buf, rr0, rb, false);
+      for (int rb = 0; rb < kPoolRows / 16; ++rb) block_step(buf, r0 + 16 * rb, rb, false);
+    } else {
+#pragma unroll 1
+      for (int rb = 0; rb < kPoolRows / 16; ++rb) {
+        const int rr0 = r0 + 16 * rb;
+        if (rr0 + 15 < wkey0 || rr0 >= prefix) continue;  // no key of the wave is visible
+        block_step(buf, rr0, rb, wkey0 + kPoolKeysPerWave - 1 > rr0);
+      }
+    }
+    if ((s + 1) % per_tile == 0) {  // tile t complete: write its pooled scores
+      float* dst = pooled_row + (size_t)kTile * t * (t + 1) / 2;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const float v = group4_sum(colsum[kt]);
+        const int key = wkey0 + 16 * kt + n16;
+        if (qg == 0 && key < prefix) dst[key] = v;
+        colsum[kt] = 0.f;
+      }
     }
     if (s + 1 < nsteps) stash(buf ^ 1);
     __syncthreads();
     if (s + 2 < nsteps) fetch(s + 2);
-  }
-
-  const size_t ragged = prefill_ragged_len(a.n, kTile);
-  float* dst = a.pooled + (size_t)(b * a.hkv + kvh) * ragged + (size_t)kTile * t * (t + 1) / 2;
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
-    const float v = group4_sum(colsum[kt]);
-    const int key = wkey0 + 16 * kt + n16;
-    if (qg == 0 && key < prefix) dst[key] = v;
   }
 }
 
@@ -440,7 +452,8 @@ hipError_t launch_prefill_reuse(const PrefillArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_prefill_pool(const PrefillArgs& a, hipStream_t s) {
-  dim3 grid(a.tiles, (a.n + kPoolKeys - 1) / kPoolKeys, a.hkv * a.batch);
+  dim3 grid((a.tiles + kPoolTiles - 1) / kPoolTiles, (a.n + kPoolKeys - 1) / kPoolKeys,
+            a.hkv * a.batch);
   if (a.d == 128) hipLaunchKernelGGL(prefill_pool<128>, grid, dim3(64 * kPoolWaves), 0, s, a);
   else if (a.d == 64) hipLaunchKernelGGL(prefill_pool<64>, grid, dim3(64 * kPoolWaves), 0, s, a);
   else return hipErrorInvalidValue;
