@@ -16,6 +16,7 @@ value = decode attention microseconds per layer (mean of the four decode
 layers); the decode reuse-layer HBM rate and the prefill tokens/s sit beside it.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -31,6 +32,45 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, vendor figure
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores, vendor figure
 
 METRIC = "decode attn µs/layer + HBM GB/s at 32K ctx; prefill attn tokens/s at 8K"
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_decode32k_prefill8k.txt")
+CSRC = os.path.join(ROOT, "long_context_amd", "csrc")
+# library timing name -> the source file that holds its kernel
+KERNEL_SOURCE = {
+    "decode_attn_dense": "decode.hip", "decode_attn_gather": "decode.hip",
+    "decode_combine": "decode.hip", "topk_decode": "topk.hip", "topk_prefill": "topk.hip",
+    "prefill_dense": "prefill.hip", "prefill_pool": "prefill.hip", "prefill_gather": "prefill.hip",
+}
+
+
+def kernel_source_digest(name):
+    """sha256 (first 16 hex digits) over the kernel's source file, the shared
+    device headers and the build flags: a change to any of them makes stored
+    counter readings stale."""
+    h = hashlib.sha256()
+    for path in (os.path.join(CSRC, KERNEL_SOURCE[name]), os.path.join(CSRC, "device_common.hpp"),
+                 os.path.join(CSRC, "kernels.hpp"), os.path.join(ROOT, "long_context_amd", "build.py")):
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(name):
+    """HBM bytes per launch of kernel `name` from the committed FETCH_SIZE /
+    WRITE_SIZE summary, or None when there is none or its source changed since."""
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    marker = "--- per-launch traffic (json) ---"
+    if marker not in text:
+        return None
+    table = json.loads(text.split(marker, 1)[1])
+    entry = table.get("kernels", {}).get(name)
+    if entry is None or entry.get("source_digest") != kernel_source_digest(name):
+        return None
+    return entry["hbm_bytes_per_launch"]
 
 
 def bytes_of(*ts):
@@ -170,6 +210,33 @@ def cpu_baseline(dec, threads, budget_s=20.0):
                        "reuse layer, timed and scaled to whole layers")}
 
 
+def profile_pass(kind, reps):
+    """Short runs for hardware-counter passes under rocprofv3.
+
+    copy:    one plain elementwise kernel that reads 1 GiB and writes 1 GiB
+             (negation of fp32), the known-size reference for FETCH_SIZE and
+             WRITE_SIZE;
+    kernels: `reps` eager passes of the decode and prefill stacks.
+    """
+    dev = "cuda"
+    if kind == "copy":
+        a = torch.ones((1 << 30) // 4, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        torch.neg(a, out=b)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_pass": "copy", "read_bytes": 1 << 30, "write_bytes": 1 << 30}))
+        return
+    dec = DecodeStack(synth.WORKLOADS["decode_llama8b_32k"], dev)
+    pre = PrefillStack(synth.WORKLOADS["prefill_8k"], dev)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dec.run()
+        pre.run()
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_pass": "kernels", "reps": reps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -177,6 +244,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
+    ap.add_argument("--profile-pass", choices=("copy", "kernels"),
+                    help="run a short pass for rocprofv3 counters instead of the benchmark")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -185,6 +254,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs an MI355X GPU", file=sys.stderr)
         sys.exit(2)
+    if args.profile_pass:
+        profile_pass(args.profile_pass, max(args.steps, 1))
+        return
     dev = "cuda"
     lib = K.library()
     dec = DecodeStack(synth.WORKLOADS["decode_llama8b_32k"], dev)
@@ -278,7 +350,7 @@ def main():
     }
     bound, achieved, peak, unit, work = rooflines.get(dominant, rooflines["decode_attn_dense"])
     roofline = {"kernel": dominant, "bound": bound, "achieved": round(achieved, 2), "peak": peak,
-                "unit": unit, "frac": round(achieved / peak, 4), "traffic": None,
+                "unit": unit, "frac": round(achieved / peak, 4), "traffic": stored_traffic(dominant),
                 "work_per_launch": work, "avg_launch_ms": round(kern[dominant], 5)}
 
     result = {
@@ -319,7 +391,8 @@ def main():
             "prefill_gather_tflops": round(gather_tflops, 2),
             "kernel_avg_us": {n: round(v * 1e3, 2) for n, v in sorted(kern.items())},
             "rooflines": {n: {"bound": r[0], "achieved": round(r[1], 2), "peak": r[2], "unit": r[3],
-                              "frac": round(r[1] / r[2], 4)} for n, r in rooflines.items()},
+                              "frac": round(r[1] / r[2], 4), "traffic": stored_traffic(n)}
+                          for n, r in rooflines.items()},
         },
     }
     if not args.no_cpu_baseline:
