@@ -10,6 +10,7 @@ namespace kascade {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint16_t u16;
 
 constexpr int kWave = 64;
@@ -37,6 +38,21 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // 4*(l/16) .. 4*(l/16)+3 of column l % 16.
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// One v_mfma_f32_32x32x16_bf16: C[32x32] += A[32x16] * B[16x32].
+// Lane l supplies row (l % 32) of A and column (l % 32) of B, each as the 8
+// contraction elements 8*(l/32) .. 8*(l/32)+7. Lane l receives column l % 32,
+// element i holding row 8*(i/4) + 4*(l/32) + (i%4).
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero_f32x16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
 }
 
 __device__ __forceinline__ bf16x8 load_bf16x8(const u16* p) {

@@ -33,7 +33,11 @@ int validate(const kascade_problem* p, int op) {
     return KASCADE_ERR_INVALID;
   if (p->num_q_heads % p->num_kv_heads != 0) return KASCADE_ERR_INVALID;
   if (p->dtype != KASCADE_F32 && p->dtype != KASCADE_BF16) return KASCADE_ERR_INVALID;
-  if (!(p->scale <= 0.0f) && !(p->scale > 0.0f)) return KASCADE_ERR_INVALID;  // NaN
+  // NaN scale, tested on the bit pattern (the library is built assuming no NaN
+  // operands, so a floating-point comparison could be folded away).
+  uint32_t scale_bits;
+  memcpy(&scale_bits, &p->scale, sizeof scale_bits);
+  if ((scale_bits & 0x7f800000u) == 0x7f800000u && (scale_bits & 0x007fffffu) != 0u) return KASCADE_ERR_INVALID;
   // Index arithmetic inside the kernels uses 32-bit row numbers.
   if ((long long)p->batch * p->num_q_heads * p->q_len >= (1ll << 31) ||
       (long long)p->batch * p->num_kv_heads * p->kv_len >= (1ll << 31))

@@ -22,6 +22,8 @@
 // is added, so the scores are recomputed rather than stored. Each wave keeps
 // 64 keys of K resident as matrix-core operands and streams the tile's query
 // rows through LDS; column sums are lane-local until one final cross-lane step.
+#include <algorithm>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -139,20 +141,44 @@ __global__ __launch_bounds__(256 * NH) void prefill_attn(PrefillArgs a) {
   };
 
   // ---- one 32-key half of a staged chunk -------------------------------------
-  auto half_step = [&](int buf, int c, int sub, bool masked) __attribute__((always_inline)) {
-    f32x4 s[2][2];  // [row block][key tile]; scores, then probabilities in place
+  // Operands come from LDS ahead of use: the K fragments of a half are read
+  // before the previous half's P.V step, and the V^T fragments of a half before
+  // its softmax, so LDS latency hides behind matrix-core and ALU work.
+  auto read_k = [&](int buf, int sub, bf16x8 (&kf)[2][C]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       const __bf16* krow = &ks[buf][(32 * sub + 16 * kt + n16) * LD + 8 * qg];
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) s[rb][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int cc = 0; cc < C; ++cc) {
-        const bf16x8 ak = *reinterpret_cast<const bf16x8*>(krow + 32 * cc);
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) s[rb][kt] = mfma16x16x32(ak, bq[rb][cc], s[rb][kt]);
-      }
+      for (int cc = 0; cc < C; ++cc) kf[kt][cc] = *reinterpret_cast<const bf16x8*>(krow + 32 * cc);
     }
+  };
+  // V^T operand: lane (d = n16, group qg) needs keys 4qg..4qg+3 and
+  // 16+4qg..16+4qg+3 of the half, the order of the P^T accumulators.
+  auto read_v = [&](int buf, int sub, bf16x8 (&vf)[D / 16]) __attribute__((always_inline)) {
+    const __bf16* v0 = &vs[WITH_O ? buf : 0][(32 * sub + 4 * qg + (n16 >> 2)) * LD + 4 * (n16 & 3)];
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      const lds_bf16x4 lo = lds_read_transposed(v0 + 16 * db);
+      const lds_bf16x4 hi = lds_read_transposed(v0 + 16 * LD + 16 * db);
+      vf[db] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  };
+  auto half_step = [&](int buf, int c, int sub, bool masked, bf16x8 (&kf)[2][C])
+      __attribute__((always_inline)) {
+    bf16x8 vf[D / 16];
+    if constexpr (WITH_O) read_v(buf, sub, vf);
+    f32x4 s[2][2];  // [row block][key tile]; scores, then probabilities in place
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) s[rb][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int cc = 0; cc < C; ++cc)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) s[rb][kt] = mfma16x16x32(kf[kt][cc], bq[rb][cc], s[rb][kt]);
+    if (sub == 0) read_k(buf, 1, kf);  // the second half's operands, during this half's softmax
     if (masked) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -202,28 +228,26 @@ __global__ __launch_bounds__(256 * NH) void prefill_attn(PrefillArgs a) {
           for (int i = 0; i < D / 16; ++i) acc[rb][i] *= alpha[rb];
         }
       }
-      // V^T operand: lane (d = n16, group qg) needs keys 4qg..4qg+3 and
-      // 16+4qg..16+4qg+3 of the half, the order of the P^T accumulators.
-      const __bf16* v0 = &vs[WITH_O ? buf : 0][(32 * sub + 4 * qg + (n16 >> 2)) * LD + 4 * (n16 & 3)];
 #pragma unroll
-      for (int db = 0; db < D / 16; ++db) {
-        const lds_bf16x4 lo = lds_read_transposed(v0 + 16 * db);
-        const lds_bf16x4 hi = lds_read_transposed(v0 + 16 * LD + 16 * db);
-        const bf16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      for (int db = 0; db < D / 16; ++db)
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) acc[rb][db] = mfma16x16x32(av, pb[rb], acc[rb][db]);
-      }
+        for (int rb = 0; rb < 2; ++rb) acc[rb][db] = mfma16x16x32(vf[db], pb[rb], acc[rb][db]);
     }
   };
   auto chunk_step = [&](int buf, int c, bool masked) __attribute__((always_inline)) {
+    bf16x8 kf[2][C];
+    read_k(buf, 0, kf);
 #pragma unroll 1
-    for (int sub = 0; sub < 2; ++sub) half_step(buf, c, sub, masked);
+    for (int sub = 0; sub < 2; ++sub) half_step(buf, c, sub, masked, kf);
   };
 
-  if (nchunks > 0) {
-    fetch(0);
-    stash(0);
-  }
+  // list_len >= 1 (k >= 1 and prefix_t >= 1), so chunk 0 always exists.
+  fetch(0);
+  stash(0);
+  // Complete the Q operand loads here: a wait for them inside the loop would
+  // also wait for the prefetch of the next chunk (vector-memory counts retire
+  // in order). s_waitcnt vmcnt(0), other counters unconstrained.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
   if (nchunks > 1) fetch(1);
   for (int c = 0; c < nchunks; ++c) {
@@ -274,41 +298,43 @@ __global__ __launch_bounds__(256 * NH) void prefill_attn(PrefillArgs a) {
 constexpr int kPoolWaves = 4;
 constexpr int kPoolKeysPerWave = 64;
 constexpr int kPoolKeys = kPoolWaves * kPoolKeysPerWave;  // keys per workgroup
-constexpr int kPoolRows = 64;                             // query rows per pipeline step
+constexpr int kPoolBlocks = kTile / 16;                   // 16-row blocks per staged head
 
-#ifndef KASCADE_POOL_TILES
-#define KASCADE_POOL_TILES 1
-#endif
-constexpr int kPoolTiles = KASCADE_POOL_TILES;  // query tiles walked by one workgroup
+// Work items of one (b, KV head) are (tile t, chunk of kPoolKeys candidate keys).
+// Tile t has prefix_t candidates and ceil(prefix_t / 256) = ceil((t+1) / 2)
+// chunks (this also holds for a ragged last tile), so the items before tile t
+// number sum_{u<t} ceil((u+1)/2).
+__host__ __device__ inline int pool_items_before(int t) {
+  const int m = t / 2;
+  return (t & 1) ? (m + 1) * (m + 1) : m * (m + 1);
+}
 
 template <int D>
-__global__ __launch_bounds__(64 * kPoolWaves) void prefill_pool(PrefillArgs a) {
+__global__ __launch_bounds__(64 * kPoolWaves) void prefill_pool(PrefillArgs a, int items, int per_xcd) {
   constexpr int C = D / 32;
   constexpr int LD = D + kLdsPad;
   constexpr int THREADS = 64 * kPoolWaves;
   constexpr int VPR = D / 8;
-  constexpr int LPT = kPoolRows * VPR / THREADS;
-  constexpr int kBlocksPerTile = kTile / kPoolRows;
-  static_assert(LPT >= 1 && kPoolRows * VPR % THREADS == 0, "row block must split evenly");
-  __shared__ __attribute__((aligned(16))) __bf16 qs[2][kPoolRows * LD];
-  __shared__ __attribute__((aligned(16))) float ls[2][kPoolRows];
+  constexpr int LPT = kTile * VPR / THREADS;
+  static_assert(LPT >= 1 && kTile * VPR % THREADS == 0, "tile rows must split evenly");
+  __shared__ __attribute__((aligned(16))) __bf16 qs[2][kTile * LD];
+  __shared__ __attribute__((aligned(16))) float ls[2][kTile];
 
-  // Workgroup = (segment of kPoolTiles query tiles, chunk of kPoolKeys keys,
-  // b, KV head). Its keys stay resident while it walks the tiles of the segment
-  // that have them as candidates. Segments vary fastest, so with a multiple of
-  // 8 segments all key chunks of one segment share an XCD's L2.
-  const int seg = blockIdx.x, chunk = blockIdx.y;
+  // Workgroups go round-robin to the 8 XCDs; items are dealt so that each XCD
+  // takes a contiguous run (the chunks of a tile share its query rows in L2).
+  const int item = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (item >= items) return;
+  int t = max(0, (int)(2.0f * sqrtf((float)item)) - 1);
+  while (pool_items_before(t + 1) <= item) ++t;
+  while (t > 0 && pool_items_before(t) > item) --t;
+  const int kbase = (item - pool_items_before(t)) * kPoolKeys;
   const int kvh = blockIdx.z % a.hkv, b = blockIdx.z / a.hkv;
-  const int kbase = chunk * kPoolKeys;
-  const int t_first = max(seg * kPoolTiles, kbase / kTile);  // first tile whose prefix passes kbase
-  const int t_end = min((seg + 1) * kPoolTiles, a.tiles);
-  if (t_first >= t_end || kbase >= a.n) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int n16 = lane & 15, qg = lane >> 4;
   const int wkey0 = kbase + wave * kPoolKeysPerWave;
+  const int row0 = t * kTile;
+  const int prefix = min(row0 + kTile, a.n);
   const float sl2 = a.scale_log2;
-  const size_t ragged = prefill_ragged_len(a.n, kTile);
-  float* pooled_row = a.pooled + (size_t)(b * a.hkv + kvh) * ragged;
 
   // K^T operands of this wave's 64 keys (keys past N read row 0 and are never
   // written out).
@@ -323,30 +349,20 @@ __global__ __launch_bounds__(64 * kPoolWaves) void prefill_pool(PrefillArgs a) {
   }
   float colsum[4] = {0.f, 0.f, 0.f, 0.f};
 
-  // Steps: (tile, head of the group, 64-row block of the tile).
-  const int per_tile = a.group * kBlocksPerTile;
-  const int nsteps = (t_end - t_first) * per_tile;
-
+  // One step stages the tile's rows of one head of the group.
   bf16x8 qr[LPT];
   float lr = INFINITY;
-  auto step_rows = [&](int s, int& t, int& h, int& r0) __attribute__((always_inline)) {
-    t = t_first + s / per_tile;
-    const int w = s % per_tile;
-    h = kvh * a.group + w / kBlocksPerTile;
-    r0 = t * kTile + kPoolRows * (w % kBlocksPerTile);
-  };
-  auto fetch = [&](int s) __attribute__((always_inline)) {
-    int t, h, r0;
-    step_rows(s, t, h, r0);
+  auto fetch = [&](int step) __attribute__((always_inline)) {
+    const int h = kvh * a.group + step;
     const u16* qh = a.q + (size_t)(b * a.hq + h) * a.n * D;
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
       const int slot = tid + i * THREADS;
       const int row = slot / VPR, col = (slot % VPR) * 8;
-      qr[i] = load_bf16x8(qh + (size_t)min(r0 + row, a.n - 1) * D + col);
+      qr[i] = load_bf16x8(qh + (size_t)min(row0 + row, a.n - 1) * D + col);
     }
-    if (tid < kPoolRows) {
-      const int row = r0 + tid;
+    if (tid < kTile) {
+      const int row = row0 + tid;
       // Rows past N get +inf so that every probability they add is 0.
       lr = row < a.n ? a.lse2[(size_t)(b * a.hq + h) * a.n + row] : INFINITY;
     }
@@ -358,63 +374,94 @@ __global__ __launch_bounds__(64 * kPoolWaves) void prefill_pool(PrefillArgs a) {
       const int row = slot / VPR, col = (slot % VPR) * 8;
       *reinterpret_cast<bf16x8*>(&qs[buf][row * LD + col]) = qr[i];
     }
-    if (tid < kPoolRows) ls[buf][tid] = lr;
+    if (tid < kTile) ls[buf][tid] = lr;
   };
-  auto block_step = [&](int buf, int rr0, int rb, bool masked) __attribute__((always_inline)) {
-    bf16x8 aq[C];
+  auto read_q = [&](int buf, int rb, bf16x8 (&aq)[C], f32x4& lse) __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < C; ++c)
       aq[c] = *reinterpret_cast<const bf16x8*>(&qs[buf][(16 * rb + n16) * LD + 32 * c + 8 * qg]);
-    const f32x4 lse = *reinterpret_cast<const f32x4*>(&ls[buf][16 * rb + 4 * qg]);
+    lse = *reinterpret_cast<const f32x4*>(&ls[buf][16 * rb + 4 * qg]);
+  };
+  // S[16 rows x 64 keys] of one row block: lane holds rows 4qg..4qg+3 of key
+  // column n16 of each 16-key tile.
+  auto scores = [&](const bf16x8 (&aq)[C], f32x4 (&s)[4]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    for (int kt = 0; kt < 4; ++kt) s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < C; ++c) s = mfma16x16x32(aq[c], bk[kt][c], s);
-      const int key = wkey0 + 16 * kt + n16;
+    for (int c = 0; c < C; ++c)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float pr = fast_exp2(fmaf(s[r], sl2, -lse[r]));
-        colsum[kt] += (!masked || key <= rr0 + 4 * qg + r) ? pr : 0.f;
-      }
-    }
+      for (int kt = 0; kt < 4; ++kt) s[kt] = mfma16x16x32(aq[c], bk[kt][c], s[kt]);
+  };
+  auto accumulate = [&](const f32x4 (&s)[4], f32x4 lse) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) colsum[kt] += fast_exp2(fmaf(s[kt][r], sl2, -lse[r]));
   };
 
   fetch(0);
   stash(0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K operands in place before the loop
   __syncthreads();
-  if (nsteps > 1) fetch(1);
-  for (int s = 0; s < nsteps; ++s) {
-    const int buf = s & 1;
-    int t, h, r0;
-    step_rows(s, t, h, r0);
-    const int prefix = min((t + 1) * kTile, a.n);
-    if (wkey0 + kPoolKeysPerWave - 1 <= r0 && r0 + kPoolRows <= prefix) {
-      // Every key of the wave is visible to every row of the step: one
-      // straight-line body, so operand reads of a block overlap the previous one.
+  if (a.group > 1) fetch(1);
+  for (int step = 0; step < a.group; ++step) {
+    const int buf = step & 1;
+    if (wkey0 + kPoolKeysPerWave - 1 <= row0) {
+      // Every key of the wave is visible to every row of the tile. Three-stage
+      // pipeline over the row blocks: LDS reads two blocks ahead, matrix-core
+      // scores one block ahead, exp2 and column sums of the current block.
+      bf16x8 aq[3][C];
+      f32x4 lq[3], sc[2][4];
+      read_q(buf, 0, aq[0], lq[0]);
+      read_q(buf, 1, aq[1], lq[1]);
+      scores(aq[0], sc[0]);
 #pragma unroll
-      for (int rb = 0; rb < kPoolRows / 16; ++rb) block_step(buf, r0 + 16 * rb, rb, false);
-    } else {
+      for (int rb = 0; rb < kPoolBlocks; ++rb) {
+        if (rb + 2 < kPoolBlocks) read_q(buf, rb + 2, aq[(rb + 2) % 3], lq[(rb + 2) % 3]);
+        if (rb + 1 < kPoolBlocks) scores(aq[(rb + 1) % 3], sc[(rb + 1) & 1]);
+        accumulate(sc[rb & 1], lq[rb % 3]);
+        // Issue order: the block's LDS reads, then each matrix-core step
+        // followed by three vector-ALU instructions of the current block.
+        __builtin_amdgcn_sched_group_barrier(0x100, C + 1, 0);
+#pragma unroll
+        for (int i = 0; i < 4 * C; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        }
+      }
+    } else if (wkey0 < prefix) {
+      // Diagonal: key j counts for row i only when j <= i.
 #pragma unroll 1
-      for (int rb = 0; rb < kPoolRows / 16; ++rb) {
-        const int rr0 = r0 + 16 * rb;
+      for (int rb = 0; rb < kPoolBlocks; ++rb) {
+        const int rr0 = row0 + 16 * rb;
         if (rr0 + 15 < wkey0 || rr0 >= prefix) continue;  // no key of the wave is visible
-        block_step(buf, rr0, rb, wkey0 + kPoolKeysPerWave - 1 > rr0);
-      }
-    }
-    if ((s + 1) % per_tile == 0) {  // tile t complete: write its pooled scores
-      float* dst = pooled_row + (size_t)kTile * t * (t + 1) / 2;
+        bf16x8 aq[C];
+        f32x4 lse, s[4];
+        read_q(buf, rb, aq, lse);
+        scores(aq, s);
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const float v = group4_sum(colsum[kt]);
-        const int key = wkey0 + 16 * kt + n16;
-        if (qg == 0 && key < prefix) dst[key] = v;
-        colsum[kt] = 0.f;
+        for (int kt = 0; kt < 4; ++kt) {
+          const int key = wkey0 + 16 * kt + n16;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float pr = fast_exp2(fmaf(s[kt][r], sl2, -lse[r]));
+            colsum[kt] += key <= rr0 + 4 * qg + r ? pr : 0.f;
+          }
+        }
       }
     }
-    if (s + 1 < nsteps) stash(buf ^ 1);
+    if (step + 1 < a.group) stash(buf ^ 1);
     __syncthreads();
-    if (s + 2 < nsteps) fetch(s + 2);
+    if (step + 2 < a.group) fetch(step + 2);
+  }
+
+  const size_t ragged = prefill_ragged_len(a.n, kTile);
+  float* dst = a.pooled + (size_t)(b * a.hkv + kvh) * ragged + (size_t)kTile * t * (t + 1) / 2;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    const float v = group4_sum(colsum[kt]);
+    const int key = wkey0 + 16 * kt + n16;
+    if (qg == 0 && key < prefix) dst[key] = v;
   }
 }
 
@@ -452,10 +499,11 @@ hipError_t launch_prefill_reuse(const PrefillArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_prefill_pool(const PrefillArgs& a, hipStream_t s) {
-  dim3 grid((a.tiles + kPoolTiles - 1) / kPoolTiles, (a.n + kPoolKeys - 1) / kPoolKeys,
-            a.hkv * a.batch);
-  if (a.d == 128) hipLaunchKernelGGL(prefill_pool<128>, grid, dim3(64 * kPoolWaves), 0, s, a);
-  else if (a.d == 64) hipLaunchKernelGGL(prefill_pool<64>, grid, dim3(64 * kPoolWaves), 0, s, a);
+  const int items = pool_items_before(a.tiles);
+  const int per_xcd = (items + 7) / 8;
+  dim3 grid(8 * per_xcd, 1, a.hkv * a.batch);
+  if (a.d == 128) hipLaunchKernelGGL(prefill_pool<128>, grid, dim3(64 * kPoolWaves), 0, s, a, items, per_xcd);
+  else if (a.d == 64) hipLaunchKernelGGL(prefill_pool<64>, grid, dim3(64 * kPoolWaves), 0, s, a, items, per_xcd);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
