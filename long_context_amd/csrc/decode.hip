@@ -201,7 +201,10 @@ __global__ __launch_bounds__(256) void decode_attn_bf16(DecodeArgs a) {
 #endif
   // Streaming the whole cache (dense) keeps the next chunk in flight; the
   // short gathered lists run more wavefronts per SIMD instead.
-  if (GATHER || !KASCADE_DECODE_PREFETCH) {
+#ifndef KASCADE_GATHER_PREFETCH
+#define KASCADE_GATHER_PREFETCH 0
+#endif
+  if (GATHER ? !KASCADE_GATHER_PREFETCH : !KASCADE_DECODE_PREFETCH) {
     for (int i = 0; i < nchunk; ++i) {
       const int j0 = begin + 32 * i;
       load_stage(s0, entry_key(j0), j0);
@@ -341,42 +344,76 @@ __global__ __launch_bounds__(256) void decode_attn_f32(DecodeArgs a) {
 }
 
 // Merge per-split (max, sum, partial output) of query rows; one wave per row.
-template <bool BF16>
+// Every load is issued before any result is needed (one memory round trip):
+// lane c holds output columns 2c, 2c+1 (d = 128) or c (d = 64) of each split.
+template <bool BF16, int D>
 __global__ __launch_bounds__(256) void decode_combine(const float* part_ml, const float* part_o,
-                                                     int rows, int splits, int d, void* out,
+                                                     int rows, int splits, void* out,
                                                      float* lse, float* lse2) {
+  constexpr int E = D / 64;  // columns per lane
+  constexpr int kBatch = 16; // splits loaded per round
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + wave_id();
   if (row >= rows) return;
   const float* ml = part_ml + (size_t)row * splits * 2;
-  float M = kNegBig;
-  for (int s = lane; s < splits; s += 64) M = fmaxf(M, ml[2 * s]);
-  M = wave_max(M);
-  float L = 0.f;
-  for (int s = lane; s < splits; s += 64) L += ml[2 * s + 1] * fast_exp2(ml[2 * s] - M);
-  L = wave_sum(L);
+  const float* po = part_o + (size_t)row * splits * D + E * lane;
+  const bool want_o = out != nullptr;  // partial outputs exist only when the output is requested
+  float M = kNegBig, L = 0.f;
+  float o[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) o[e] = 0.f;
+  for (int s0 = 0; s0 < splits; s0 += kBatch) {
+    float mv[kBatch], lv[kBatch], ov[kBatch][E];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int s = min(s0 + i, splits - 1);
+      mv[i] = ml[2 * s];
+      lv[i] = ml[2 * s + 1];
+      if (!want_o) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) ov[i][e] = 0.f;
+      } else if (E == 2) {
+        const float2 v = *reinterpret_cast<const float2*>(po + (size_t)s * D);
+        ov[i][0] = v.x;
+        ov[i][E - 1] = v.y;
+      } else {
+        ov[i][0] = po[(size_t)s * D];
+      }
+    }
+    float mb = M;
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i)
+      if (s0 + i < splits) mb = fmaxf(mb, mv[i]);
+    const float alpha = fast_exp2(M - mb);
+    L *= alpha;
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] *= alpha;
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const float w = s0 + i < splits ? fast_exp2(mv[i] - mb) : 0.f;
+      L += lv[i] * w;
+#pragma unroll
+      for (int e = 0; e < E; ++e) o[e] += ov[i][e] * w;
+    }
+    M = mb;
+  }
   if (lane == 0) {
     if (lse) lse[row] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
     if (lse2) lse2[row] = M + log2f(L);
   }
   if (!out) return;
   const float inv = L > 0.f ? 1.0f / L : 0.f;
-  for (int c = lane; c < d; c += 64) {
-    float o = 0.f;
-    const float* po = part_o + (size_t)row * splits * d + c;
-    int s = 0;
-    for (; s + 4 <= splits; s += 4) {
-      const float w0 = fast_exp2(ml[2 * s] - M), w1 = fast_exp2(ml[2 * s + 2] - M);
-      const float w2 = fast_exp2(ml[2 * s + 4] - M), w3 = fast_exp2(ml[2 * s + 6] - M);
-      o += po[(size_t)s * d] * w0 + po[(size_t)(s + 1) * d] * w1 + po[(size_t)(s + 2) * d] * w2 +
-           po[(size_t)(s + 3) * d] * w3;
-    }
-    for (; s < splits; ++s) o += po[(size_t)s * d] * fast_exp2(ml[2 * s] - M);
-    o *= inv;
-    if (BF16)
-      static_cast<u16*>(out)[(size_t)row * d + c] = float_to_bf16_bits(o);
+  if (BF16) {
+    u16* dst = static_cast<u16*>(out) + (size_t)row * D + E * lane;
+    if (E == 2)
+      *reinterpret_cast<uint32_t*>(dst) =
+          float_to_bf16_bits(o[0] * inv) | ((uint32_t)float_to_bf16_bits(o[E - 1] * inv) << 16);
     else
-      static_cast<float*>(out)[(size_t)row * d + c] = o;
+      dst[0] = float_to_bf16_bits(o[0] * inv);
+  } else {
+    float* dst = static_cast<float*>(out) + (size_t)row * D + E * lane;
+#pragma unroll
+    for (int e = 0; e < E; ++e) dst[e] = o[e] * inv;
   }
 }
 
@@ -416,12 +453,16 @@ hipError_t launch_decode_combine(const float* part_ml, const float* part_o, int 
                                  int d, bool bf16, void* out, float* lse, float* lse2,
                                  hipStream_t s) {
   const dim3 grid((rows + 3) / 4), block(256);
-  if (bf16)
-    hipLaunchKernelGGL(decode_combine<true>, grid, block, 0, s, part_ml, part_o, rows, splits, d,
-                       out, lse, lse2);
-  else
-    hipLaunchKernelGGL(decode_combine<false>, grid, block, 0, s, part_ml, part_o, rows, splits, d,
-                       out, lse, lse2);
+#define KASCADE_COMBINE(B_, D_) \
+  hipLaunchKernelGGL((decode_combine<B_, D_>), grid, block, 0, s, part_ml, part_o, rows, splits, out, lse, lse2)
+  if (d == 128) {
+    if (bf16) KASCADE_COMBINE(true, 128); else KASCADE_COMBINE(false, 128);
+  } else if (d == 64) {
+    if (bf16) KASCADE_COMBINE(true, 64); else KASCADE_COMBINE(false, 64);
+  } else {
+    return hipErrorInvalidValue;
+  }
+#undef KASCADE_COMBINE
   return hipGetLastError();
 }
 
