@@ -63,10 +63,15 @@ __global__ __launch_bounds__(256 * NH) void prefill_attn(PrefillArgs a) {
   __shared__ int keys_s[2][kKeyChunk];
   __shared__ int info_s[2][4];  // gather mode: smallest valid key, largest key, any padding
 
-  const int t = a.tiles - 1 - blockIdx.x;  // longest tiles first
-  const int b = blockIdx.z;
+  // Longest tiles first across all heads and batches: workgroup i takes tile
+  // tiles-1 - i / (B * Hq/NH), so the dispatcher hands out the work in
+  // decreasing length and the last workgroups to start are the shortest.
+  const int units = a.batch * (a.hq / NH);
+  const int t = a.tiles - 1 - (int)blockIdx.x / units;
+  const int b = ((int)blockIdx.x % units) / (a.hq / NH);
+  const int hb = (int)blockIdx.x % (a.hq / NH);
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-  const int h = blockIdx.y * NH + wave / 4;
+  const int h = hb * NH + wave / 4;
   const int kvh = h / a.group;             // the NH heads of a block share one KV head
   const int n16 = lane & 15, qg = lane >> 4;
   const int prefix = min((t + 1) * kTile, a.n);
@@ -476,10 +481,10 @@ template <int D, bool GATHER, bool WITH_O>
 hipError_t launch_attn(const PrefillArgs& a, hipStream_t s) {
   // Two heads of a GQA group per workgroup share every staged K/V chunk.
   if (a.group % 2 == 0) {
-    dim3 grid(a.tiles, a.hq / 2, a.batch);
+    dim3 grid(a.tiles * a.batch * (a.hq / 2));
     hipLaunchKernelGGL((prefill_attn<D, GATHER, WITH_O, 2>), grid, dim3(512), 0, s, a);
   } else {
-    dim3 grid(a.tiles, a.hq, a.batch);
+    dim3 grid(a.tiles * a.batch * a.hq);
     hipLaunchKernelGGL((prefill_attn<D, GATHER, WITH_O, 1>), grid, dim3(256), 0, s, a);
   }
   return hipGetLastError();
