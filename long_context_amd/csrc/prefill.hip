@@ -31,7 +31,6 @@ namespace kascade {
 
 namespace {
 
-constexpr int kKeyChunk = 64;      // keys staged per pipeline step
 constexpr int kRowsPerWave = 32;   // query rows per wavefront in prefill_attn
 constexpr int kTile = 128;         // query tile: four wavefronts of 32 rows
 constexpr int kLdsPad = 16;        // bf16 elements of padding per LDS row
@@ -50,8 +49,11 @@ __device__ __forceinline__ lds_bf16x4 lds_read_transposed(const __bf16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_vec*)(p));
 }
 
-template <int D, bool GATHER, bool WITH_O, int NH>
+// KC keys are staged per pipeline step (64 or 128).
+template <int D, bool GATHER, bool WITH_O, int NH, int KC>
 __global__ __launch_bounds__(256 * NH) void prefill_attn(PrefillArgs a) {
+  constexpr int kKeyChunk = KC;
+  constexpr int kKeyWaves = KC / 64;  // wavefronts that hold the chunk's list entries
   constexpr int C = D / 32;
   constexpr int LD = D + kLdsPad;
   constexpr int THREADS = 256 * NH;
@@ -61,7 +63,8 @@ __global__ __launch_bounds__(256 * NH) void prefill_attn(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) __bf16 ks[2][kKeyChunk * LD];
   __shared__ __attribute__((aligned(16))) __bf16 vs[WITH_O ? 2 : 1][WITH_O ? kKeyChunk * LD : 8];
   __shared__ int keys_s[2][kKeyChunk];
-  __shared__ int info_s[2][4];  // gather mode: smallest valid key, largest key, any padding
+  // gather mode, per key-holding wavefront: smallest valid key, largest key, any padding
+  __shared__ int info_s[2][kKeyWaves][4];
 
   // Longest tiles first across all heads and batches: workgroup i takes tile
   // tiles-1 - i / (B * Hq/NH), so the dispatcher hands out the work in
@@ -108,17 +111,29 @@ __global__ __launch_bounds__(256 * NH) void prefill_attn(PrefillArgs a) {
     int key = pos < list_len ? (GATHER ? list[pos] : pos) : -1;
     return key < a.n ? key : -1;  // entries outside the sequence are skipped
   };
+  // Gather mode reads a chunk's list entries one fetch ahead (next_keys), so
+  // the row loads of a fetch never wait on the list.
+  int next_keys[LPT];
+  int next_key_reg = -1;
+  auto load_keys = [&](int c) __attribute__((always_inline)) {
+    if (GATHER) {
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) next_keys[i] = key_at(c * kKeyChunk + (tid + i * THREADS) / VPR);
+      if (tid < kKeyChunk) next_key_reg = key_at(c * kKeyChunk + tid);
+    }
+  };
   auto fetch = [&](int c) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
       const int slot = tid + i * THREADS;
       const int row = slot / VPR, col = (slot % VPR) * 8;
-      const int key = key_at(c * kKeyChunk + row);
+      const int key = GATHER ? next_keys[i] : key_at(c * kKeyChunk + row);
       const size_t src = (size_t)(key < 0 ? 0 : key) * D + col;
       kr[i] = load_bf16x8(kb + src);
       if (WITH_O) vr[i] = load_bf16x8(vb + src);
     }
-    if (GATHER && tid < kKeyChunk) key_reg = key_at(c * kKeyChunk + tid);
+    if (GATHER && tid < kKeyChunk) key_reg = next_key_reg;
+    if (GATHER && (c + 1) * kKeyChunk < list_len) load_keys(c + 1);
   };
   auto stash = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
@@ -128,8 +143,8 @@ __global__ __launch_bounds__(256 * NH) void prefill_attn(PrefillArgs a) {
       *reinterpret_cast<bf16x8*>(&ks[buf][row * LD + col]) = kr[i];
       if (WITH_O) *reinterpret_cast<bf16x8*>(&vs[buf][row * LD + col]) = vr[i];
     }
-    if (GATHER && wave == 0) {  // wave 0 holds the chunk's 64 keys, one per lane
-      keys_s[buf][lane] = key_reg;
+    if (GATHER && wave < kKeyWaves) {  // these waves hold the chunk's keys, one per lane
+      keys_s[buf][tid] = key_reg;
       int lo = key_reg >= 0 ? key_reg : 0x7fffffff, hi = key_reg;
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) {
@@ -138,9 +153,9 @@ __global__ __launch_bounds__(256 * NH) void prefill_attn(PrefillArgs a) {
       }
       const bool pad = __any(key_reg < 0);
       if (lane == 0) {
-        info_s[buf][0] = lo;
-        info_s[buf][1] = hi;
-        info_s[buf][2] = pad;
+        info_s[buf][wave][0] = lo;
+        info_s[buf][wave][1] = hi;
+        info_s[buf][wave][2] = pad;
       }
     }
   };
@@ -183,7 +198,7 @@ __global__ __launch_bounds__(256 * NH) void prefill_attn(PrefillArgs a) {
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) s[rb][kt] = mfma16x16x32(kf[kt][cc], bq[rb][cc], s[rb][kt]);
-    if (sub == 0) read_k(buf, 1, kf);  // the second half's operands, during this half's softmax
+    if (sub + 1 < KC / 32) read_k(buf, sub + 1, kf);  // the next half's operands, during this half's softmax
     if (masked) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -243,10 +258,11 @@ __global__ __launch_bounds__(256 * NH) void prefill_attn(PrefillArgs a) {
     bf16x8 kf[2][C];
     read_k(buf, 0, kf);
 #pragma unroll 1
-    for (int sub = 0; sub < 2; ++sub) half_step(buf, c, sub, masked, kf);
+    for (int sub = 0; sub < KC / 32; ++sub) half_step(buf, c, sub, masked, kf);
   };
 
   // list_len >= 1 (k >= 1 and prefix_t >= 1), so chunk 0 always exists.
+  load_keys(0);
   fetch(0);
   stash(0);
   // Complete the Q operand loads here: a wait for them inside the loop would
@@ -261,9 +277,15 @@ __global__ __launch_bounds__(256 * NH) void prefill_attn(PrefillArgs a) {
       int vmin, vmax;
       bool pad;
       if (GATHER) {
-        vmin = info_s[buf][0];
-        vmax = info_s[buf][1];
-        pad = info_s[buf][2] != 0;
+        vmin = info_s[buf][0][0];
+        vmax = info_s[buf][0][1];
+        pad = info_s[buf][0][2] != 0;
+#pragma unroll
+        for (int w = 1; w < kKeyWaves; ++w) {
+          vmin = min(vmin, info_s[buf][w][0]);
+          vmax = max(vmax, info_s[buf][w][1]);
+          pad = pad || info_s[buf][w][2] != 0;
+        }
       } else {
         vmin = c * kKeyChunk;
         vmax = min(vmin + kKeyChunk, list_len) - 1;
@@ -479,13 +501,16 @@ __global__ void lse2_to_lse_kernel(const float* lse2, float* lse, size_t count) 
 
 template <int D, bool GATHER, bool WITH_O>
 hipError_t launch_attn(const PrefillArgs& a, hipStream_t s) {
-  // Two heads of a GQA group per workgroup share every staged K/V chunk.
-  if (a.group % 2 == 0) {
+  // Reuse layers: two heads of a GQA group per workgroup share every gathered
+  // K/V chunk, staged 128 keys at a time so each gather has a long step of
+  // work to land behind. Dense pass: one head per workgroup and 64-key steps,
+  // two workgroups per compute unit.
+  if (GATHER && a.group % 2 == 0) {
     dim3 grid(a.tiles * a.batch * (a.hq / 2));
-    hipLaunchKernelGGL((prefill_attn<D, GATHER, WITH_O, 2>), grid, dim3(512), 0, s, a);
+    hipLaunchKernelGGL((prefill_attn<D, GATHER, WITH_O, 2, 128>), grid, dim3(512), 0, s, a);
   } else {
     dim3 grid(a.tiles * a.batch * a.hq);
-    hipLaunchKernelGGL((prefill_attn<D, GATHER, WITH_O, 1>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((prefill_attn<D, GATHER, WITH_O, 1, 64>), grid, dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }
