@@ -82,9 +82,19 @@ __global__ __launch_bounds__(256) void decode_attn_bf16(DecodeArgs a) {
     for (int s = 0; s < 8; ++s)
       sel[half][s] = static_cast<__bf16>((8 * qg + s == 16 * half + n) ? 1.0f : 0.0f);
 
-  const int begin = split * a.keys_per_split;
-  const int end = min(begin + a.keys_per_split, a.list_len);
-  const int nchunk = (end - begin + 31) / 32;
+#ifndef KASCADE_DENSE_INTERLEAVE
+#define KASCADE_DENSE_INTERLEAVE 1
+#endif
+  // Gather mode: split s walks list entries [s*kps, min((s+1)*kps, len)).
+  // Dense mode: the splits of a (b, KV head) take its 32-key chunks in turn
+  // (split s: chunks s, s + splits, ...), so together they sweep the cache
+  // front to back in step rather than each streaming a region of its own.
+  constexpr bool kInterleave = !GATHER && KASCADE_DENSE_INTERLEAVE;
+  const int begin = kInterleave ? 32 * split : split * a.keys_per_split;
+  const int end = kInterleave ? a.list_len : min(begin + a.keys_per_split, a.list_len);
+  const int stride = kInterleave ? 32 * a.splits : 32;  // keys between a split's chunks
+  const int nchunk = kInterleave ? (begin < end ? (end - begin + stride - 1) / stride : 0)
+                                 : (end - begin + 31) / 32;
 
   // Gather mode: lane l reads list entry j0 + (l & 31); rows and validity of
   // the chunk follow by lane exchange, so each entry is read once.
@@ -206,7 +216,7 @@ __global__ __launch_bounds__(256) void decode_attn_bf16(DecodeArgs a) {
 #endif
   if (GATHER ? !KASCADE_GATHER_PREFETCH : !KASCADE_DECODE_PREFETCH) {
     for (int i = 0; i < nchunk; ++i) {
-      const int j0 = begin + 32 * i;
+      const int j0 = begin + stride * i;
       load_stage(s0, entry_key(j0), j0);
       compute(s0, j0);
     }
@@ -215,20 +225,20 @@ __global__ __launch_bounds__(256) void decode_attn_bf16(DecodeArgs a) {
   // list entries) before chunk i is computed.
   int kn = entry_key(begin);
   load_stage(s0, kn, begin);
-  kn = entry_key(begin + 32);
+  kn = entry_key(begin + stride);
   for (int i = 0; i < nchunk; i += 2) {
-    const int j0 = begin + 32 * i;
+    const int j0 = begin + stride * i;
     if (i + 1 < nchunk) {
-      load_stage(s1, kn, j0 + 32);
-      kn = entry_key(j0 + 64);
+      load_stage(s1, kn, j0 + stride);
+      kn = entry_key(j0 + 2 * stride);
     }
     compute(s0, j0);
     if (i + 1 >= nchunk) break;
     if (i + 2 < nchunk) {
-      load_stage(s0, kn, j0 + 64);
-      kn = entry_key(j0 + 96);
+      load_stage(s0, kn, j0 + 2 * stride);
+      kn = entry_key(j0 + 3 * stride);
     }
-    compute(s1, j0 + 32);
+    compute(s1, j0 + stride);
   }
   }
 

@@ -18,7 +18,13 @@ constexpr size_t kAlign = 256;
 #ifndef KASCADE_TARGET_WAVES
 #define KASCADE_TARGET_WAVES 2048
 #endif
-constexpr int kTargetWaves = KASCADE_TARGET_WAVES;  // about eight wavefronts per compute unit
+#ifndef KASCADE_TARGET_WAVES_DENSE
+#define KASCADE_TARGET_WAVES_DENSE 4096
+#endif
+// Split-K decode: wavefronts to aim for: about eight per compute unit for the
+// gathered lists, sixteen for the anchor's sweep over the whole cache.
+constexpr int kTargetWaves = KASCADE_TARGET_WAVES;
+constexpr int kTargetWavesDense = KASCADE_TARGET_WAVES_DENSE;
 constexpr int kMaxGroup = 16;       // query heads per KV head handled together
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -62,10 +68,11 @@ struct DecodeSplit {
 
 // Spread a list of `len` keys per (b, KV head) over enough wavefronts to fill
 // the chip; each wavefront gets a multiple of 64 keys.
-DecodeSplit decode_split(const kascade_problem* p, int len) {
+DecodeSplit decode_split(const kascade_problem* p, int len, bool dense) {
   const int units = p->batch * p->num_kv_heads;
   const int max_splits = (len + 63) / 64;
-  int splits = (kTargetWaves + units - 1) / units;
+  const int target = dense ? kTargetWavesDense : kTargetWaves;
+  int splits = (target + units - 1) / units;
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;
   int kps = (len + splits - 1) / splits;
@@ -81,7 +88,7 @@ struct DecodeWorkspace {
 DecodeWorkspace decode_workspace(const kascade_problem* p, int op) {
   DecodeWorkspace w{};
   const bool anchor = op == KASCADE_OP_ANCHOR_DECODE;
-  w.split = decode_split(p, anchor ? p->kv_len : p->top_k);
+  w.split = decode_split(p, anchor ? p->kv_len : p->top_k, anchor);
   const size_t rows = (size_t)p->batch * p->num_q_heads;
   size_t off = 0;
   w.part_ml = off;
