@@ -69,10 +69,15 @@ __global__ __launch_bounds__(256 * NH) void prefill_attn(PrefillArgs a) {
   // Longest tiles first across all heads and batches: workgroup i takes tile
   // tiles-1 - i / (B * Hq/NH), so the dispatcher hands out the work in
   // decreasing length and the last workgroups to start are the shortest.
+  // Within a tile, u % (B*Hkv) is the (b, KV head) and u / (B*Hkv) the head
+  // block of its group: consecutive workgroups, which the dispatcher deals to
+  // the 8 XCDs in turn, keep a KV group's head blocks on one XCD and its L2.
   const int units = a.batch * (a.hq / NH);
   const int t = a.tiles - 1 - (int)blockIdx.x / units;
-  const int b = ((int)blockIdx.x % units) / (a.hq / NH);
-  const int hb = (int)blockIdx.x % (a.hq / NH);
+  const int u = (int)blockIdx.x % units;
+  const int kvg = u % (a.batch * a.hkv), member = u / (a.batch * a.hkv);
+  const int b = kvg / a.hkv;
+  const int hb = (kvg % a.hkv) * (a.group / NH) + member;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int h = hb * NH + wave / 4;
   const int kvh = h / a.group;             // the NH heads of a block share one KV head
