@@ -338,6 +338,12 @@ def main():
     dense_tflops = 2 * pre.qk_flops() / (kern["prefill_dense"] * 1e-3) / 1e12
     gather_tflops = pre.reuse_flops() / (kern["prefill_gather"] * 1e-3) / 1e12
 
+    # dense attention per layer: the anchor's dense pass with output (decode:
+    # the cache stream, which also writes the scaled logits, plus the split
+    # merge; prefill: causal flash attention with output and lse)
+    dense_dec_ms = kern["decode_attn_dense"] + kern["decode_combine"]
+    dense_pre_ms = kern["prefill_dense"]
+
     # dominant kernel: the largest share of the step
     per_step = {n: kernels[n][0] / args.steps for n in kernels}
     dominant = max(per_step, key=per_step.get)
@@ -384,6 +390,16 @@ def main():
             "decode_reuse_hbm_gbs_call": round(reuse_call_gbs, 1),
             "decode_anchor_hbm_gbs_kernel": round(anchor_gbs, 1),
             "prefill_tokens_per_s": round(prefill_tps, 1),
+            # context: dense attention (the anchor's dense pass with output)
+            # per layer against the Kascade stack's mean layer
+            "dense_decode_layer_us": round(dense_dec_ms * 1e3, 2),
+            "decode_speedup_vs_dense": round(dense_dec_ms / t_dec_layer_ms, 3),
+            "dense_prefill_layer_us": round(dense_pre_ms * 1e3, 2),
+            "prefill_speedup_vs_dense": round(dense_pre_ms / (t_pre_stack_ms / wp.layers), 3),
+            "speedup_vs_dense_by_layers": {
+                str(L): {"decode": round(L * dense_dec_ms / (avg["decode_anchor"] + (L - 1) * avg["decode_reuse"]), 3),
+                         "prefill": round(L * dense_pre_ms / (avg["prefill_anchor"] + (L - 1) * avg["prefill_reuse"]), 3)}
+                for L in (2, 4, 8, 16, 32)},
             "prefill_anchor_us": round(avg["prefill_anchor"] * 1e3, 2),
             "prefill_reuse_us": round(avg["prefill_reuse"] * 1e3, 2),
             "prefill_pool_tflops": round(pool_tflops, 2),

@@ -50,18 +50,36 @@ __device__ __forceinline__ lds_bf16x4 lds_read_transposed(const __bf16* p) {
 }
 
 // KC keys are staged per pipeline step (64 or 128).
+//
+// Matrix-core layout (v_mfma_f32_32x32x16_bf16). A wavefront owns 32 query
+// rows; lane l serves row wrow0 + (l % 32) and lane half hf = l / 32.
+//   S^T[key, row] += K[key, d-chunk] . Q^T[d-chunk, row]: the A operand is
+//   key (kb0 + l%32) with d slice 16c + 8hf; the B operand (Q, resident) is
+//   row l%32 with the same slice. Lane l receives its row's scores for keys
+//   kb0 + 8(i/4) + 4hf + (i%4), i = 0..15, so a row's maximum is lane-local
+//   plus one exchange with lane l^32.
+//   O^T[d, row] += V^T[d, keys] . P^T[keys, row], 16 keys per step ks: the
+//   B operand takes the lane's own probabilities i = 8ks .. 8ks+7, so slot j of
+//   half hf stands for key 16ks + 8(j/4) + 4hf + (j%4); the A operand supplies
+//   V at those keys for d = 32db + l%32, two transposed LDS reads of four
+//   consecutive keys each.
 template <int D, bool GATHER, bool WITH_O, int NH, int KC>
 __global__ __launch_bounds__(256 * NH) void prefill_attn(PrefillArgs a) {
   constexpr int kKeyChunk = KC;
   constexpr int kKeyWaves = KC / 64;  // wavefronts that hold the chunk's list entries
-  constexpr int C = D / 32;
-  constexpr int LD = D + kLdsPad;
+  constexpr int C = D / 16;           // 16-element contraction chunks of S^T
+  constexpr int DB = D / 32;          // 32-row blocks of O^T
+  constexpr int LD = D + kLdsPad;        // K rows: 16-byte operand reads spread over the banks
+  // V rows: a transposed read fetches four consecutive rows at 64 consecutive
+  // bytes (two 16-lane groups), so rows are padded by 64 bytes (16 banks):
+  // the four rows then cover all 64 banks.
+  constexpr int LDV = D + 32;
   constexpr int THREADS = 256 * NH;
   constexpr int VPR = D / 8;                             // 16-byte vectors per row
   constexpr int LPT = kKeyChunk * VPR / THREADS;         // vectors per thread per tensor
   static_assert(LPT >= 1 && kKeyChunk * VPR % THREADS == 0, "chunk must split evenly");
   __shared__ __attribute__((aligned(16))) __bf16 ks[2][kKeyChunk * LD];
-  __shared__ __attribute__((aligned(16))) __bf16 vs[WITH_O ? 2 : 1][WITH_O ? kKeyChunk * LD : 8];
+  __shared__ __attribute__((aligned(16))) __bf16 vs[WITH_O ? 2 : 1][WITH_O ? kKeyChunk * LDV : 8];
   __shared__ int keys_s[2][kKeyChunk];
   // gather mode, per key-holding wavefront: smallest valid key, largest key, any padding
   __shared__ int info_s[2][kKeyWaves][4];
@@ -81,10 +99,11 @@ __global__ __launch_bounds__(256 * NH) void prefill_attn(PrefillArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int h = hb * NH + wave / 4;
   const int kvh = h / a.group;             // the NH heads of a block share one KV head
-  const int n16 = lane & 15, qg = lane >> 4;
+  const int col = lane & 31, hf = lane >> 5;
   const int prefix = min((t + 1) * kTile, a.n);
   const int wrow0 = t * kTile + (wave & 3) * kRowsPerWave;
   const int wrow_last = min(wrow0 + kRowsPerWave, a.n) - 1;
+  const int my_row = wrow0 + col;
   const float sl2 = a.scale_log2;
 
   const u16* kb = a.k + (size_t)(b * a.hkv + kvh) * a.n * D;
@@ -93,21 +112,17 @@ __global__ __launch_bounds__(256 * NH) void prefill_attn(PrefillArgs a) {
   const int list_len = GATHER ? min(a.topk, prefix) : prefix;
   const int nchunks = (list_len + kKeyChunk - 1) / kKeyChunk;
 
-  bf16x8 bq[2][C];
+  bf16x8 bq[C];
+  {
+    const u16* qrow = a.q + ((size_t)(b * a.hq + h) * a.n + min(my_row, a.n - 1)) * D;
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int row = min(wrow0 + 16 * rb + n16, a.n - 1);
-    const u16* qrow = a.q + ((size_t)(b * a.hq + h) * a.n + row) * D;
-#pragma unroll
-    for (int c = 0; c < C; ++c) bq[rb][c] = load_bf16x8(qrow + 32 * c + 8 * qg);
+    for (int c = 0; c < C; ++c) bq[c] = load_bf16x8(qrow + 16 * c + 8 * hf);
   }
 
-  float m[2] = {kNegBig, kNegBig}, l[2] = {0.f, 0.f};
-  f32x4 acc[2][D / 16];
+  float m = kNegBig, l = 0.f;
+  f32x16 acc[DB];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int i = 0; i < D / 16; ++i) acc[rb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < DB; ++i) acc[i] = zero_f32x16();
 
   // ---- staging: chunk c's rows go global -> registers -> LDS ----------------
   bf16x8 kr[LPT], vr[LPT];
@@ -131,9 +146,9 @@ __global__ __launch_bounds__(256 * NH) void prefill_attn(PrefillArgs a) {
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
       const int slot = tid + i * THREADS;
-      const int row = slot / VPR, col = (slot % VPR) * 8;
+      const int row = slot / VPR, colv = (slot % VPR) * 8;
       const int key = GATHER ? next_keys[i] : key_at(c * kKeyChunk + row);
-      const size_t src = (size_t)(key < 0 ? 0 : key) * D + col;
+      const size_t src = (size_t)(key < 0 ? 0 : key) * D + colv;
       kr[i] = load_bf16x8(kb + src);
       if (WITH_O) vr[i] = load_bf16x8(vb + src);
     }
@@ -144,9 +159,9 @@ __global__ __launch_bounds__(256 * NH) void prefill_attn(PrefillArgs a) {
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
       const int slot = tid + i * THREADS;
-      const int row = slot / VPR, col = (slot % VPR) * 8;
-      *reinterpret_cast<bf16x8*>(&ks[buf][row * LD + col]) = kr[i];
-      if (WITH_O) *reinterpret_cast<bf16x8*>(&vs[buf][row * LD + col]) = vr[i];
+      const int row = slot / VPR, colv = (slot % VPR) * 8;
+      *reinterpret_cast<bf16x8*>(&ks[buf][row * LD + colv]) = kr[i];
+      if (WITH_O) *reinterpret_cast<bf16x8*>(&vs[buf][row * LDV + colv]) = vr[i];
     }
     if (GATHER && wave < kKeyWaves) {  // these waves hold the chunk's keys, one per lane
       keys_s[buf][tid] = key_reg;
@@ -165,105 +180,93 @@ __global__ __launch_bounds__(256 * NH) void prefill_attn(PrefillArgs a) {
     }
   };
 
-  // ---- one 32-key half of a staged chunk -------------------------------------
-  // Operands come from LDS ahead of use: the K fragments of a half are read
-  // before the previous half's P.V step, and the V^T fragments of a half before
-  // its softmax, so LDS latency hides behind matrix-core and ALU work.
-  auto read_k = [&](int buf, int sub, bf16x8 (&kf)[2][C]) __attribute__((always_inline)) {
+  // ---- one 32-key step of a staged chunk -------------------------------------
+  // Operands come from LDS ahead of use: the K fragments of a step are read
+  // before the previous step's P.V, and the V^T fragments of a step before its
+  // softmax, so LDS latency hides behind matrix-core and ALU work.
+  auto read_k = [&](int buf, int sub, bf16x8 (&kf)[C]) __attribute__((always_inline)) {
+    const __bf16* krow = &ks[buf][(32 * sub + col) * LD + 8 * hf];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const __bf16* krow = &ks[buf][(32 * sub + 16 * kt + n16) * LD + 8 * qg];
-#pragma unroll
-      for (int cc = 0; cc < C; ++cc) kf[kt][cc] = *reinterpret_cast<const bf16x8*>(krow + 32 * cc);
-    }
+    for (int c = 0; c < C; ++c) kf[c] = *reinterpret_cast<const bf16x8*>(krow + 16 * c);
   };
-  // V^T operand: lane (d = n16, group qg) needs keys 4qg..4qg+3 and
-  // 16+4qg..16+4qg+3 of the half, the order of the P^T accumulators.
-  auto read_v = [&](int buf, int sub, bf16x8 (&vf)[D / 16]) __attribute__((always_inline)) {
-    const __bf16* v0 = &vs[WITH_O ? buf : 0][(32 * sub + 4 * qg + (n16 >> 2)) * LD + 4 * (n16 & 3)];
+  // V^T operand of d block db and key step s2: lane group g = l/16 reads, for
+  // d = 32db + 16(g%2) + (l%16), keys 16s2 + 4hf + 0..3 and 16s2 + 8 + 4hf + 0..3
+  // (row base + L/4, columns 4(L%4) of the lane's transposed read).
+  auto read_v = [&](int buf, int sub, bf16x8 (&vf)[DB][2]) __attribute__((always_inline)) {
+    const int L = lane & 15, g = lane >> 4;
+    const __bf16* v0 = &vs[WITH_O ? buf : 0][(32 * sub + 4 * (g >> 1) + (L >> 2)) * LDV + 16 * (g & 1) + 4 * (L & 3)];
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db) {
-      const lds_bf16x4 lo = lds_read_transposed(v0 + 16 * db);
-      const lds_bf16x4 hi = lds_read_transposed(v0 + 16 * LD + 16 * db);
-      vf[db] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    }
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const lds_bf16x4 lo = lds_read_transposed(v0 + (16 * s2) * LDV + 32 * db);
+        const lds_bf16x4 hi = lds_read_transposed(v0 + (16 * s2 + 8) * LDV + 32 * db);
+        vf[db][s2] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
   };
-  auto half_step = [&](int buf, int c, int sub, bool masked, bf16x8 (&kf)[2][C])
-      __attribute__((always_inline)) {
-    bf16x8 vf[D / 16];
+  auto step = [&](int buf, int c, int sub, bool masked, bf16x8 (&kf)[C]) __attribute__((always_inline)) {
+    bf16x8 vf[DB][2];
     if constexpr (WITH_O) read_v(buf, sub, vf);
-    f32x4 s[2][2];  // [row block][key tile]; scores, then probabilities in place
+    f32x16 s = zero_f32x16();
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) s[rb][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int cc = 0; cc < C; ++cc)
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) s[rb][kt] = mfma16x16x32(kf[kt][cc], bq[rb][cc], s[rb][kt]);
-    if (sub + 1 < KC / 32) read_k(buf, sub + 1, kf);  // the next half's operands, during this half's softmax
+    for (int cc = 0; cc < C; ++cc) s = mfma32x32x16(kf[cc], bq[cc], s);
+    if (sub + 1 < KC / 32) read_k(buf, sub + 1, kf);  // next step's operands, during this softmax
     if (masked) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int pos = c * kKeyChunk + 32 * sub + 16 * kt + 4 * qg + r;
-          const int key = GATHER ? keys_s[buf][pos - c * kKeyChunk] : (pos < list_len ? pos : -1);
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb)
-            if (key < 0 || key > wrow0 + 16 * rb + n16) s[rb][kt][r] = -INFINITY;
-        }
-    }
-    float alpha[2];
-    bool rescale[2];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      float cmax = fmaxf(fmaxf(fmaxf(s[rb][0][0], s[rb][0][1]), fmaxf(s[rb][0][2], s[rb][0][3])),
-                         fmaxf(fmaxf(s[rb][1][0], s[rb][1][1]), fmaxf(s[rb][1][2], s[rb][1][3])));
-      cmax = group4_max(cmax) * sl2;
-      // Lazy rescaling: keep the reference maximum unless some row's maximum
-      // grew by more than 2^8; probabilities then stay below 256 in fp32.
-      alpha[rb] = 1.0f;
-      rescale[rb] = __any(cmax > m[rb] + kRescaleLog2);
-      if (rescale[rb]) {
-        const float mnew = fmaxf(m[rb], cmax);
-        alpha[rb] = fast_exp2(m[rb] - mnew);
-        m[rb] = mnew;
+      for (int i = 0; i < 16; ++i) {
+        const int kk = 32 * sub + 8 * (i >> 2) + 4 * hf + (i & 3);  // key slot in the chunk
+        const int key = GATHER ? keys_s[buf][kk] : (c * kKeyChunk + kk < list_len ? c * kKeyChunk + kk : -1);
+        if (key < 0 || key > my_row) s[i] = -INFINITY;
       }
-      const float neg_m = -m[rb];
-      float lsum = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          s[rb][kt][r] = fast_exp2(fmaf(s[rb][kt][r], sl2, neg_m));
-          lsum += s[rb][kt][r];
-        }
-      l[rb] = l[rb] * alpha[rb] + lsum;
     }
-    if (WITH_O) {
+    float cmax = s[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) cmax = fmaxf(cmax, s[i]);
+    {
+      float lo_, hi_;
+      pair32(cmax, lo_, hi_);
+      cmax = fmaxf(lo_, hi_) * sl2;
+    }
+    // Lazy rescaling: keep the reference maximum unless some row's maximum
+    // grew by more than 2^8; probabilities then stay below 256 in fp32.
+    float alpha = 1.0f;
+    const bool rescale = __any(cmax > m + kRescaleLog2);
+    if (rescale) {
+      const float mnew = fmaxf(m, cmax);
+      alpha = fast_exp2(m - mnew);
+      m = mnew;
+    }
+    const float neg_m = -m;
+    float lsum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      s[i] = fast_exp2(fmaf(s[i], sl2, neg_m));
+      lsum += s[i];
+    }
+    l = l * alpha + lsum;
+    if constexpr (WITH_O) {
       bf16x8 pb[2];
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        pb[rb] = pack_bf16x8(s[rb][0], s[rb][1]);
-        if (rescale[rb]) {
+      for (int s2 = 0; s2 < 2; ++s2) {
+        f32x4 p0 = {s[8 * s2 + 0], s[8 * s2 + 1], s[8 * s2 + 2], s[8 * s2 + 3]};
+        f32x4 p1 = {s[8 * s2 + 4], s[8 * s2 + 5], s[8 * s2 + 6], s[8 * s2 + 7]};
+        pb[s2] = pack_bf16x8(p0, p1);
+      }
+      if (rescale) {
 #pragma unroll
-          for (int i = 0; i < D / 16; ++i) acc[rb][i] *= alpha[rb];
-        }
+        for (int i = 0; i < DB; ++i) acc[i] *= alpha;
       }
 #pragma unroll
-      for (int db = 0; db < D / 16; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) acc[rb][db] = mfma16x16x32(vf[db], pb[rb], acc[rb][db]);
+        for (int s2 = 0; s2 < 2; ++s2) acc[db] = mfma32x32x16(vf[db][s2], pb[s2], acc[db]);
     }
   };
   auto chunk_step = [&](int buf, int c, bool masked) __attribute__((always_inline)) {
-    bf16x8 kf[2][C];
+    bf16x8 kf[C];
     read_k(buf, 0, kf);
 #pragma unroll 1
-    for (int sub = 0; sub < KC / 32; ++sub) half_step(buf, c, sub, masked, kf);
+    for (int sub = 0; sub < KC / 32; ++sub) step(buf, c, sub, masked, kf);
   };
 
   // list_len >= 1 (k >= 1 and prefix_t >= 1), so chunk 0 always exists.
@@ -304,23 +307,26 @@ __global__ __launch_bounds__(256 * NH) void prefill_attn(PrefillArgs a) {
     if (c + 2 < nchunks) fetch(c + 2);
   }
 
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const float lt = group4_sum(l[rb]);
-    const int row = wrow0 + 16 * rb + n16;
-    if (row >= a.n) continue;
-    const size_t orow = (size_t)(b * a.hq + h) * a.n + row;
-    if (!GATHER && qg == 0) a.lse2[orow] = m[rb] + log2f(lt);
-    if (WITH_O) {
+  // Row totals: each lane half summed its own keys.
+  float lo_, hi_;
+  pair32(l, lo_, hi_);
+  const float lt = lo_ + hi_;
+  if (my_row < a.n) {
+    const size_t orow = (size_t)(b * a.hq + h) * a.n + my_row;
+    if (!GATHER && hf == 0) a.lse2[orow] = m + log2f(lt);
+    if constexpr (WITH_O) {
+      // acc[db] element i is d = 32db + 8(i/4) + 4hf + (i%4) of this row.
       const float inv = lt > 0.f ? 1.0f / lt : 0.f;
 #pragma unroll
-      for (int db = 0; db < D / 16; ++db) {
-        u16 o4[4];
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o4[r] = float_to_bf16_bits(acc[rb][db][r] * inv);
-        *reinterpret_cast<uint2*>(a.out + orow * D + 16 * db + 4 * qg) =
-            make_uint2(o4[0] | (uint32_t(o4[1]) << 16), o4[2] | (uint32_t(o4[3]) << 16));
-      }
+        for (int q = 0; q < 4; ++q) {
+          u16 o4[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o4[r] = float_to_bf16_bits(acc[db][4 * q + r] * inv);
+          *reinterpret_cast<uint2*>(a.out + orow * D + 32 * db + 8 * q + 4 * hf) =
+              make_uint2(o4[0] | (uint32_t(o4[1]) << 16), o4[2] | (uint32_t(o4[3]) << 16));
+        }
     }
   }
 }
