@@ -228,3 +228,70 @@ def reuse_prefill(q, k, v, idx, q_tile=128, out=None, ws=None, scale=0.0, stream
     lib.check(lib.reuse_prefill_raw(prob, _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(out), wp, wb,
                                     _stream(stream)), "kascade_reuse_prefill")
     return out
+
+
+# ---- a stack of layers with an anchor schedule ------------------------------
+
+def anchor_schedule(n_layers, anchors):
+    """Role of each layer under an anchor list: ("dense", None) before the first
+    anchor, ("anchor", l) for an anchor layer l, ("reuse", a) for a layer that
+    reuses the indices of the nearest preceding anchor a (Kascade abstract on
+    the opentrain.ai page, "Abstract"; the summary's interface line takes a
+    top-k and a list of anchor layers, "Practical Implications")."""
+    anchors = sorted(set(int(a) for a in anchors))
+    if not anchors:
+        raise ValueError("at least one anchor layer is needed")
+    if anchors[0] < 0 or anchors[-1] >= n_layers:
+        raise ValueError(f"anchor layers must lie in [0, {n_layers})")
+    roles, last = [], None
+    for l in range(n_layers):
+        if l in anchors:
+            last = l
+            roles.append(("anchor", l))
+        elif last is None:
+            roles.append(("dense", None))
+        else:
+            roles.append(("reuse", last))
+    return roles
+
+
+def kascade_attention(qs, ks, vs, top_k, anchors, q_tile=128, outs=None, scale=0.0, stream=None):
+    """Kascade attention over a stack of layers, one call per layer through the
+    C ABI. qs, ks, vs: per-layer tensors, decode (Q [B,Hq,1,d]) or causal
+    prefill (Q [B,Hq,N,d]), K/V [B,Hkv,N,d]. Layers before the first anchor
+    attend densely (the anchor call's dense output; its indices are not kept),
+    an anchor layer outputs dense attention and saves its top-k indices, every
+    other layer attends only to the saved indices of the nearest preceding
+    anchor, with its own Q, K and V. Returns (per-layer outputs,
+    {anchor layer: idx})."""
+    n_layers = len(qs)
+    if not (len(ks) == len(vs) == n_layers):
+        raise ValueError("qs, ks and vs must have one tensor per layer")
+    roles = anchor_schedule(n_layers, anchors)
+    decode = qs[0].shape[2] == 1
+    n = ks[0].shape[2]
+    if outs is None:
+        outs = [torch.empty_like(q) for q in qs]
+    saved, ws_anchor, ws_reuse = {}, None, None
+    for l, (role, src) in enumerate(roles):
+        q, k, v = qs[l], ks[l], vs[l]
+        if role in ("dense", "anchor"):
+            kk = min(top_k, n) if (decode or role == "dense") else top_k
+            if decode:
+                if ws_anchor is None:
+                    ws_anchor = workspace(problem(q, k, kk, 1, scale), OP_ANCHOR_DECODE, q.device)
+                idx = anchor_decode(q, k, v, kk, out=outs[l], ws=ws_anchor, scale=scale, stream=stream)
+            else:
+                if ws_anchor is None:
+                    ws_anchor = workspace(problem(q, k, kk, q_tile, scale), OP_ANCHOR_PREFILL, q.device)
+                idx = anchor_prefill(q, k, v, kk, q_tile, out=outs[l], ws=ws_anchor, scale=scale,
+                                     stream=stream)
+            if role == "anchor":
+                saved[l] = idx
+        elif decode:
+            if ws_reuse is None:
+                ws_reuse = workspace(problem(q, k, top_k, 1, scale), OP_REUSE_DECODE, q.device)
+            reuse_decode(q, k, v, saved[src], out=outs[l], ws=ws_reuse, scale=scale, stream=stream)
+        else:
+            reuse_prefill(q, k, v, saved[src], q_tile, out=outs[l], scale=scale, stream=stream)
+    return outs, saved
