@@ -18,6 +18,7 @@ layers); the decode reuse-layer HBM rate and the prefill tokens/s sit beside it.
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -237,6 +238,134 @@ def profile_pass(kind, reps):
     print(json.dumps({"profile_pass": "kernels", "reps": reps}), flush=True)
 
 
+# ---- accuracy against dense attention, swept over k -------------------------
+#
+# The pages leave k as a hyper-parameter picked with a small validation sweep
+# (euno.news summary, "Limitations & Future Work") and fix the prefill
+# selection to tiles (Kascade abstract, opentrain.ai page). This sweep runs the
+# path at k = N/64 ... N/4 over a stack of synthetic layers whose planted heavy
+# keys drift from layer to layer, and reports per layer how well the anchor's
+# index set serves it against that layer's own dense attention.
+
+SWEEP_K_FRACTIONS = (64, 32, 16, 8, 4)     # k = N / f
+
+
+def pooled_decode(q, k):
+    """Group-mean post-softmax attention of each KV head's decode queries over
+    all keys, float32 [B, Hkv, N]."""
+    B, Hq, _, d = q.shape
+    Hkv = k.shape[1]
+    qf = q.float().reshape(B, Hkv, Hq // Hkv, d)
+    kt = k.float().transpose(2, 3).contiguous()
+    return torch.softmax(torch.matmul(qf, kt) / math.sqrt(d), dim=-1).mean(dim=2)
+
+
+def pooled_prefill(q, k, tile):
+    """Causal post-softmax attention averaged over each query tile's rows and
+    the group's heads, float32 [B, Hkv, tiles, N]; row t sums to 1."""
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    tiles = -(-N // tile)
+    tile_of_row = torch.arange(N, device=q.device) // tile
+    rows = torch.bincount(tile_of_row, minlength=tiles).float()
+    future = torch.ones((N, N), dtype=torch.bool, device=q.device).triu(1)
+    out = torch.zeros((B, Hkv, tiles, N), dtype=torch.float32, device=q.device)
+    for b in range(B):
+        for kv in range(Hkv):
+            s = torch.matmul(q[b, kv * G:(kv + 1) * G].float(), k[b, kv].float().t().contiguous())
+            s = (s / math.sqrt(d)).masked_fill_(future, float("-inf"))
+            p = torch.softmax(s, dim=-1).sum(0)
+            out[b, kv].index_add_(0, tile_of_row, p)
+            del s, p
+    return out / (G * rows)[None, None, :, None]
+
+
+def captured_mass(pooled, idx):
+    """Mean over index sets of the pooled attention mass the set holds
+    (entries -1 hold none). pooled [..., N], idx [..., k] with equal leading dims."""
+    take = pooled.gather(-1, idx.long().clamp_min(0)) * (idx >= 0)
+    return float(take.sum(-1).mean())
+
+
+def planted_recall(positions, idx, tile, n):
+    """Mean over (b, KV head, tile) of the fraction of planted keys inside the
+    tile's causal prefix that the index set holds. positions[b][kv] are one
+    layer's planted rows; idx [B, Hkv, tiles, k] on the host."""
+    fr = []
+    for b, per_kv in enumerate(positions):
+        for kv, pos in enumerate(per_kv):
+            for t in range(idx.shape[2]):
+                live = pos[pos < min((t + 1) * tile, n)] if idx.shape[2] > 1 else pos
+                if live.size:
+                    fr.append(np.isin(live, idx[b, kv, t]).mean())
+    return float(np.mean(fr))
+
+
+def rel_error(out, ref):
+    """Frobenius-norm error of `out` relative to `ref`, in float32."""
+    o, r = out.float(), ref.float()
+    return float(torch.linalg.vector_norm(o - r) / torch.linalg.vector_norm(r))
+
+
+def accuracy_sweep(w, fractions=SWEEP_K_FRACTIONS, dev="cuda"):
+    """For each k = N/f: the anchor (layer 0) selects its index sets once, then
+    every layer of the stack (the anchor itself included) attends through the
+    reuse call to those sets with its own Q, K and V. Per layer: planted-key
+    recall, captured pooled attention mass, and the output's error relative to
+    the layer's dense attention. Returns one dict per k."""
+    decode = w.phase == "decode"
+    pos = synth.planted_positions(w)
+    layers = [synth.make_layer(w, l, dev, pos) for l in range(w.layers)]
+    dense, pooled = [], []
+    for q, k, v in layers:
+        o = torch.empty_like(q)
+        if decode:
+            K.anchor_decode(q, k, v, min(w.k, w.n), out=o)
+            pooled.append(pooled_decode(q, k).unsqueeze(2))
+        else:
+            K.anchor_prefill(q, k, v, min(w.k, w.n), w.tile, out=o)
+            pooled.append(pooled_prefill(q, k, w.tile))
+        dense.append(o)
+    rows = []
+    q0, k0, v0 = layers[0]
+    for f in fractions:
+        kk = max(1, w.n // f)
+        if decode:
+            idx = K.anchor_decode(q0, k0, v0, kk)
+        else:
+            idx = K.anchor_prefill(q0, k0, v0, kk, w.tile)
+        idx_host = idx.cpu().numpy()
+        per_layer = []
+        for l, (q, k, v) in enumerate(layers):
+            if decode:
+                o = K.reuse_decode(q, k, v, idx)
+            else:
+                o = K.reuse_prefill(q, k, v, idx, w.tile)
+            per_layer.append({
+                "layer": l,
+                "planted_recall": round(planted_recall(pos[l], idx_host, w.tile, w.n), 4),
+                "attention_mass": round(captured_mass(pooled[l], idx), 4),
+                "rel_error_vs_dense": round(rel_error(o, dense[l]), 5),
+            })
+        rows.append({"sweep": "accuracy_vs_k", "workload": w.name, "phase": w.phase, "n": w.n,
+                     "q_tile": w.tile if not decode else None, "top_k": kk, "k_over_n": f"1/{f}",
+                     "share": w.share, "gain": w.gain, "layers": per_layer})
+    torch.cuda.synchronize()
+    return rows
+
+
+def sweep_workloads():
+    """The decode workload at 32K and the 8K prefill workload, the latter with
+    its planted keys drifting like the decode one's (70 % kept from layer to
+    layer) so the reuse layers meet new heavy keys; each at the benchmarked
+    planted-row gain (diffuse attention) and at gain 16 (most of the attention
+    on the planted keys)."""
+    dec = synth.WORKLOADS["decode_llama8b_32k"]
+    pre = synth.WORKLOADS["prefill_8k"].scaled(share=0.7)
+    return [dec, dec.scaled(gain=16.0), pre, pre.scaled(gain=16.0)]
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -246,6 +375,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
     ap.add_argument("--profile-pass", choices=("copy", "kernels"),
                     help="run a short pass for rocprofv3 counters instead of the benchmark")
+    ap.add_argument("--sweep", action="store_true",
+                    help="accuracy against dense attention over k = N/64 ... N/4 (one JSON line per k)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -256,6 +387,11 @@ def main():
         sys.exit(2)
     if args.profile_pass:
         profile_pass(args.profile_pass, max(args.steps, 1))
+        return
+    if args.sweep:
+        for w in sweep_workloads():
+            for row in accuracy_sweep(w):
+                print(json.dumps(row), flush=True)
         return
     dev = "cuda"
     lib = K.library()

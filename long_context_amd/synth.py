@@ -15,9 +15,12 @@ Recipe (all normal draws are float32, then rounded to nearest-even bfloat16
 unless the workload is float32):
   * Q, K, V ~ N(0, 1); generator seed 1000*workload_id + 10*layer + tensor_id
     (tensor_id 0 = Q, 1 = K, 2 = V, 3 = planted-row noise).
-  * decode planted row p of KV head kv:  K[b,kv,p] = 4 * q_dir + N(0, 0.1^2),
+  * decode planted row p of KV head kv:  K[b,kv,p] = gain * q_dir + N(0, 0.1^2),
     q_dir the unit vector of the sum of the group's query vectors at that layer.
-  * prefill planted row p:  K[b,kv,p] *= 4;  sink rows 0..3:  K[b,kv,0:4] *= 3.
+  * prefill planted row p:  K[b,kv,p] *= gain;  sink rows 0..3:  K[b,kv,0:4] *= 3.
+  * gain = 4 for the workloads below; at d = 128 and 32K keys that leaves the
+    attention diffuse (the planted keys hold a few per cent of it), a larger
+    gain concentrates it on them.
   * positions come from numpy.random.default_rng(1000*workload_id + 7 + b):
     `share` = 1.0 keeps them for every layer, 0.7 keeps round(0.7*P) of the
     previous layer's P positions and redraws the rest disjoint from the kept.
@@ -45,6 +48,7 @@ class Workload:
     planted: int        # planted heavy keys per KV head
     share: float        # fraction of planted positions kept layer to layer
     sinks: int = 0      # leading sink rows (prefill)
+    gain: float = 4.0   # planted-row scale
 
     @property
     def group(self):
@@ -130,9 +134,9 @@ def make_layer(w: Workload, layer: int, device="cpu", positions=None):
                     qsum = q[b, kv * w.group:(kv + 1) * w.group, 0, :].sum(0)
                     qdir = qsum / qsum.norm()
                     eps = 0.1 * torch.randn((pos.numel(), w.d), generator=noise_gen, device=dev)
-                    k[b, kv, pos, :] = 4.0 * qdir[None, :] + eps
+                    k[b, kv, pos, :] = w.gain * qdir[None, :] + eps
                 else:
-                    k[b, kv, pos, :] *= 4.0
+                    k[b, kv, pos, :] *= w.gain
     if w.sinks:
         k[:, :, : w.sinks, :] *= 3.0
     dt = w.torch_dtype
