@@ -30,6 +30,7 @@ class OracleProblem(ctypes.Structure):
         ("q_tile", ctypes.c_int),
         ("scale", ctypes.c_double),
         ("dtype", ctypes.c_int),
+        ("shared_index_set", ctypes.c_int),
     ]
 
 
@@ -45,6 +46,15 @@ def _as_input(x):
     if x.dtype in (np.uint16, np.int16):
         return x.view(np.uint16), 1
     raise TypeError(f"oracle inputs must be float32 or bf16 bits, got {x.dtype}")
+
+
+def _check_sets(idx, p, shared):
+    """The oracle reads idx as [B, S, tiles, k]; refuse a smaller array."""
+    sets = 1 if shared else p.num_kv_heads
+    tiles = 1 if p.q_len == 1 else -(-p.kv_len // p.q_tile)
+    if idx.size != p.batch * sets * tiles * p.top_k:
+        raise ValueError(f"idx holds {idx.size} entries, expected [B={p.batch}, S={sets}, tiles={tiles}, "
+                         f"k={p.top_k}]")
 
 
 def _units(units, width):
@@ -77,26 +87,28 @@ class Oracle:
         self.lib = lib
 
     @staticmethod
-    def problem(q, k, top_k=1, q_tile=128, scale=None, dtype=0):
+    def problem(q, k, top_k=1, q_tile=128, scale=None, dtype=0, shared=False):
         B, Hq, L, d = q.shape
         _, Hkv, N, _ = k.shape
         if scale is None:
             scale = 1.0 / np.sqrt(d)
-        return OracleProblem(B, Hq, Hkv, d, L, N, int(top_k), int(q_tile), float(scale), dtype)
+        return OracleProblem(B, Hq, Hkv, d, L, N, int(top_k), int(q_tile), float(scale), dtype,
+                             int(bool(shared)))
 
     def _check(self, rc, name):
         if rc != 0:
             raise ValueError(f"{name} failed with status {rc}")
 
     # -- anchor -------------------------------------------------------------
-    def anchor_decode(self, q, k, top_k, units=None, scale=None, threads=0, want_pooled=True):
-        """q [B,Hq,1,d], k [B,Hkv,N,d] -> (idx [U,k], pooled [U,N] or None), U = units or B*Hkv."""
+    def anchor_decode(self, q, k, top_k, units=None, scale=None, threads=0, want_pooled=True, shared=False):
+        """q [B,Hq,1,d], k [B,Hkv,N,d] -> (idx [U,k], pooled [U,N] or None), U = units (b, set)
+        or B*S, S = Hkv (one set per KV head) or 1 (shared=True: one set for all heads)."""
         q, dt = _as_input(q)
         k, dt2 = _as_input(k)
         assert dt == dt2
-        p = self.problem(q, k, top_k, 1, scale, dt)
+        p = self.problem(q, k, top_k, 1, scale, dt, shared)
         u, nu = _units(units, 2)
-        n = nu if u is not None else p.batch * p.num_kv_heads
+        n = nu if u is not None else p.batch * (1 if shared else p.num_kv_heads)
         idx = np.empty((n, top_k), np.int32)
         pooled = np.empty((n, p.kv_len), np.float64) if want_pooled else None
         rc = self.lib.oracle_anchor_decode(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(u, _c_int_p), nu,
@@ -104,15 +116,17 @@ class Oracle:
         self._check(rc, "oracle_anchor_decode")
         return idx, pooled
 
-    def anchor_prefill(self, q, k, top_k, q_tile, units=None, scale=None, threads=0, want_pooled=True):
-        """q [B,Hq,N,d], k [B,Hkv,N,d] -> (idx [U,k], pooled [U,N]), U = units (b,kv,t) or all."""
+    def anchor_prefill(self, q, k, top_k, q_tile, units=None, scale=None, threads=0, want_pooled=True,
+                       shared=False):
+        """q [B,Hq,N,d], k [B,Hkv,N,d] -> (idx [U,k], pooled [U,N]), U = units (b,set,t) or all
+        B*S*tiles, S = Hkv or 1 (shared=True)."""
         q, dt = _as_input(q)
         k, dt2 = _as_input(k)
         assert dt == dt2
-        p = self.problem(q, k, top_k, q_tile, scale, dt)
+        p = self.problem(q, k, top_k, q_tile, scale, dt, shared)
         u, nu = _units(units, 3)
         tiles = -(-p.kv_len // q_tile)
-        n = nu if u is not None else p.batch * p.num_kv_heads * tiles
+        n = nu if u is not None else p.batch * (1 if shared else p.num_kv_heads) * tiles
         idx = np.empty((n, top_k), np.int32)
         pooled = np.empty((n, p.kv_len), np.float64) if want_pooled else None
         rc = self.lib.oracle_anchor_prefill(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(u, _c_int_p), nu,
@@ -121,13 +135,14 @@ class Oracle:
         return idx, pooled
 
     # -- reuse --------------------------------------------------------------
-    def reuse_decode(self, q, k, v, idx, units=None, scale=None, threads=0):
-        """idx [B,Hkv,1,k] -> out [U,d], U = units (b,h) or B*Hq."""
+    def reuse_decode(self, q, k, v, idx, units=None, scale=None, threads=0, shared=False):
+        """idx [B,S,1,k] (S = Hkv, or 1 with shared=True) -> out [U,d], U = units (b,h) or B*Hq."""
         q, dt = _as_input(q)
         k, _ = _as_input(k)
         v, _ = _as_input(v)
         idx = np.ascontiguousarray(idx, dtype=np.int32)
-        p = self.problem(q, k, idx.shape[-1], 1, scale, dt)
+        p = self.problem(q, k, idx.shape[-1], 1, scale, dt, shared)
+        _check_sets(idx, p, shared)
         u, nu = _units(units, 2)
         n = nu if u is not None else p.batch * p.num_q_heads
         out = np.empty((n, p.head_dim), np.float64)
@@ -136,13 +151,14 @@ class Oracle:
         self._check(rc, "oracle_reuse_decode")
         return out
 
-    def reuse_prefill(self, q, k, v, idx, q_tile, units=None, scale=None, threads=0):
-        """idx [B,Hkv,tiles,k] -> out [U,d], U = units (b,h,i) or B*Hq*N."""
+    def reuse_prefill(self, q, k, v, idx, q_tile, units=None, scale=None, threads=0, shared=False):
+        """idx [B,S,tiles,k] (S = Hkv, or 1 with shared=True) -> out [U,d], U = units (b,h,i) or B*Hq*N."""
         q, dt = _as_input(q)
         k, _ = _as_input(k)
         v, _ = _as_input(v)
         idx = np.ascontiguousarray(idx, dtype=np.int32)
-        p = self.problem(q, k, idx.shape[-1], q_tile, scale, dt)
+        p = self.problem(q, k, idx.shape[-1], q_tile, scale, dt, shared)
+        _check_sets(idx, p, shared)
         u, nu = _units(units, 3)
         n = nu if u is not None else p.batch * p.num_q_heads * p.q_len
         out = np.empty((n, p.head_dim), np.float64)

@@ -42,7 +42,32 @@ static int problem_ok(const oracle_problem* p) {
   if (p->num_q_heads % p->num_kv_heads != 0) return 0;
   if (p->q_len < 1 || p->kv_len < 1 || p->top_k < 1) return 0;
   if (p->dtype != 0 && p->dtype != 1) return 0;
+  if (p->shared_index_set != 0 && p->shared_index_set != 1) return 0;
   return 1;
+}
+
+/* Index sets per batch row: one per KV head (head-aware selection), or one
+ * shared by every head (the non-head-aware ablation). */
+static int index_sets(const oracle_problem* p) {
+  return p->shared_index_set ? 1 : p->num_kv_heads;
+}
+
+/* The index set that query head h attends through. */
+static int set_of_head(const oracle_problem* p, int h) {
+  return p->shared_index_set ? 0 : h / (p->num_q_heads / p->num_kv_heads);
+}
+
+/* The query heads whose probabilities are pooled into index set `set`:
+ * heads h0 .. h0+nh-1 (the KV head's group, or all heads for a shared set). */
+static void pooled_heads(const oracle_problem* p, int set, int* h0, int* nh) {
+  const int G = p->num_q_heads / p->num_kv_heads;
+  if (p->shared_index_set) {
+    *h0 = 0;
+    *nh = p->num_q_heads;
+  } else {
+    *h0 = set * G;
+    *nh = G;
+  }
 }
 
 static size_t q_offset(const oracle_problem* p, int b, int h, int i) {
@@ -129,8 +154,8 @@ int oracle_anchor_decode(const oracle_problem* p, const void* q, const void* k,
                          int32_t* idx_out, double* pooled_out, int nthreads) {
   if (!problem_ok(p) || p->q_len != 1 || p->top_k > p->kv_len || !q || !k || !idx_out)
     return ERR_PROBLEM;
-  const int G = p->num_q_heads / p->num_kv_heads, N = p->kv_len;
-  const int total = p->batch * p->num_kv_heads;
+  const int G = p->num_q_heads / p->num_kv_heads, N = p->kv_len, S = index_sets(p);
+  const int total = p->batch * S;
   const int n = units ? nunits : total;
   int status = 0;
   set_threads(nthreads);
@@ -140,18 +165,20 @@ int oracle_anchor_decode(const oracle_problem* p, const void* q, const void* k,
     double* pooled = (double*)malloc((size_t)N * sizeof(double));
 #pragma omp for schedule(dynamic, 1)
     for (int u = 0; u < n; ++u) {
-      int b = units ? units[2 * u] : u / p->num_kv_heads;
-      int kvh = units ? units[2 * u + 1] : u % p->num_kv_heads;
+      int b = units ? units[2 * u] : u / S;
+      int set = units ? units[2 * u + 1] : u % S;
       if (!s || !pooled) { fail(&status, ERR_NOMEM); continue; }
-      if (b < 0 || b >= p->batch || kvh < 0 || kvh >= p->num_kv_heads) { fail(&status, ERR_UNIT); continue; }
+      if (b < 0 || b >= p->batch || set < 0 || set >= S) { fail(&status, ERR_UNIT); continue; }
+      int h0, nh;
+      pooled_heads(p, set, &h0, &nh);
       for (int j = 0; j < N; ++j) pooled[j] = 0.0;
-      for (int g = 0; g < G; ++g) {
-        int h = kvh * G + g;  /* query heads of one group are contiguous */
-        for (int j = 0; j < N; ++j) s[j] = logit(p, q, k, b, h, 0, kvh, j);
+      for (int h = h0; h < h0 + nh; ++h) {
+        /* query head h reads KV head h / G; a group's heads are contiguous */
+        for (int j = 0; j < N; ++j) s[j] = logit(p, q, k, b, h, 0, h / G, j);
         softmax_inplace(s, N);
         for (int j = 0; j < N; ++j) pooled[j] += s[j];
       }
-      for (int j = 0; j < N; ++j) pooled[j] /= G;
+      for (int j = 0; j < N; ++j) pooled[j] /= nh;
       if (select_top_k(pooled, N, p->top_k, idx_out + (size_t)u * p->top_k)) fail(&status, ERR_NOMEM);
       if (pooled_out) memcpy(pooled_out + (size_t)u * N, pooled, (size_t)N * sizeof(double));
     }
@@ -168,9 +195,9 @@ int oracle_anchor_prefill(const oracle_problem* p, const void* q, const void* k,
                           int32_t* idx_out, double* pooled_out, int nthreads) {
   if (!problem_ok(p) || p->q_len != p->kv_len || p->q_tile < 1 || !q || !k || !idx_out)
     return ERR_PROBLEM;
-  const int G = p->num_q_heads / p->num_kv_heads, N = p->kv_len, T = p->q_tile;
+  const int G = p->num_q_heads / p->num_kv_heads, N = p->kv_len, T = p->q_tile, S = index_sets(p);
   const int tiles = (N + T - 1) / T;
-  const int total = p->batch * p->num_kv_heads * tiles;
+  const int total = p->batch * S * tiles;
   const int n = units ? nunits : total;
   int status = 0;
   set_threads(nthreads);
@@ -180,33 +207,34 @@ int oracle_anchor_prefill(const oracle_problem* p, const void* q, const void* k,
     double* pooled = (double*)malloc((size_t)N * sizeof(double));
 #pragma omp for schedule(dynamic, 1)
     for (int u = 0; u < n; ++u) {
-      int b, kvh, t;
+      int b, set, t;
       if (units) {
-        b = units[3 * u]; kvh = units[3 * u + 1]; t = units[3 * u + 2];
+        b = units[3 * u]; set = units[3 * u + 1]; t = units[3 * u + 2];
       } else {
-        b = u / (p->num_kv_heads * tiles);
-        kvh = (u / tiles) % p->num_kv_heads;
+        b = u / (S * tiles);
+        set = (u / tiles) % S;
         t = u % tiles;
       }
       if (!s || !pooled) { fail(&status, ERR_NOMEM); continue; }
-      if (b < 0 || b >= p->batch || kvh < 0 || kvh >= p->num_kv_heads || t < 0 || t >= tiles) {
+      if (b < 0 || b >= p->batch || set < 0 || set >= S || t < 0 || t >= tiles) {
         fail(&status, ERR_UNIT);
         continue;
       }
       const int row0 = t * T;
       const int prefix = (t + 1) * T < N ? (t + 1) * T : N; /* rows of the tile end here too */
       const int rows = prefix - row0;
+      int h0, nh;
+      pooled_heads(p, set, &h0, &nh);
       for (int j = 0; j < N; ++j) pooled[j] = 0.0;
-      for (int g = 0; g < G; ++g) {
-        int h = kvh * G + g;
+      for (int h = h0; h < h0 + nh; ++h) {
         for (int i = row0; i < prefix; ++i) {
           /* causal row i sees keys 0..i */
-          for (int j = 0; j <= i; ++j) s[j] = logit(p, q, k, b, h, i, kvh, j);
+          for (int j = 0; j <= i; ++j) s[j] = logit(p, q, k, b, h, i, h / G, j);
           softmax_inplace(s, i + 1);
           for (int j = 0; j <= i; ++j) pooled[j] += s[j];
         }
       }
-      for (int j = 0; j < prefix; ++j) pooled[j] /= (double)G * rows;
+      for (int j = 0; j < prefix; ++j) pooled[j] /= (double)nh * rows;
       if (select_top_k(pooled, prefix, p->top_k, idx_out + (size_t)u * p->top_k)) fail(&status, ERR_NOMEM);
       if (pooled_out) memcpy(pooled_out + (size_t)u * N, pooled, (size_t)N * sizeof(double));
     }
@@ -243,7 +271,7 @@ int oracle_reuse_decode(const oracle_problem* p, const void* q, const void* k, c
                         const int32_t* idx, const int32_t* units, int nunits,
                         double* out, int nthreads) {
   if (!problem_ok(p) || p->q_len != 1 || !q || !k || !v || !idx || !out) return ERR_PROBLEM;
-  const int G = p->num_q_heads / p->num_kv_heads, N = p->kv_len, K = p->top_k;
+  const int N = p->kv_len, K = p->top_k;
   const int total = p->batch * p->num_q_heads;
   const int n = units ? nunits : total;
   int status = 0;
@@ -258,7 +286,7 @@ int oracle_reuse_decode(const oracle_problem* p, const void* q, const void* k, c
       int h = units ? units[2 * u + 1] : u % p->num_q_heads;
       if (!s || !keys) { fail(&status, ERR_NOMEM); continue; }
       if (b < 0 || b >= p->batch || h < 0 || h >= p->num_q_heads) { fail(&status, ERR_UNIT); continue; }
-      const int32_t* list = idx + ((size_t)b * p->num_kv_heads + h / G) * K;
+      const int32_t* list = idx + ((size_t)b * index_sets(p) + set_of_head(p, h)) * K;
       int nk = 0;
       for (int a = 0; a < K; ++a) {
         if (list[a] == -1) continue;             /* padding */
@@ -281,7 +309,7 @@ int oracle_reuse_prefill(const oracle_problem* p, const void* q, const void* k, 
                          double* out, int nthreads) {
   if (!problem_ok(p) || p->q_len != p->kv_len || p->q_tile < 1 || !q || !k || !v || !idx || !out)
     return ERR_PROBLEM;
-  const int G = p->num_q_heads / p->num_kv_heads, N = p->kv_len, K = p->top_k, T = p->q_tile;
+  const int N = p->kv_len, K = p->top_k, T = p->q_tile;
   const int tiles = (N + T - 1) / T;
   const int total = p->batch * p->num_q_heads * N;
   const int n = units ? nunits : total;
@@ -307,7 +335,7 @@ int oracle_reuse_prefill(const oracle_problem* p, const void* q, const void* k, 
         continue;
       }
       const int t = i / T;
-      const int32_t* list = idx + (((size_t)b * p->num_kv_heads + h / G) * tiles + t) * K;
+      const int32_t* list = idx + (((size_t)b * index_sets(p) + set_of_head(p, h)) * tiles + t) * K;
       int nk = 0;
       for (int a = 0; a < K; ++a) {
         if (list[a] == -1) continue;

@@ -23,6 +23,11 @@
  *  - Reuse layer: softmax attention restricted to the saved index set, with
  *    the reuse layer's own Q, K and V (summary, Methodology step 3). Prefill
  *    rows also obey causality: row i uses only saved keys j <= i.
+ *  - Non-head-aware variant (shared_index_set = 1), the ablation the pages
+ *    compare head-aware selection against (summary, "Key Contributions" and
+ *    "Results & Findings"): one index set per batch row (and tile), ranking the mean of
+ *    the post-softmax probabilities of all Hq query heads, and every head
+ *    reuses that one set. With Hkv = 1 it is the head-aware case.
  *  - Dense: textbook softmax attention (causal for prefill), used for the
  *    k = N identity and for the anchor layer's optional dense output.
  *
@@ -33,7 +38,8 @@
  *
  * Conventions shared with the GPU library by specification only (no code):
  *   Q, O : [B, Hq, q_len, d] row-major    K, V : [B, Hkv, kv_len, d]
- *   idx  : [B, Hkv, tiles, k] int32, ascending, -1 after the first k_t slots
+ *   idx  : [B, S, tiles, k] int32, ascending, -1 after the first k_t slots,
+ *          S = Hkv (one set per KV head) or 1 (one shared set)
  *   query head h reads KV head h / G, G = Hq / Hkv.
  * Element type: dtype 0 = float32, dtype 1 = bfloat16 stored as uint16 bits.
  * Everything is converted exactly to double and computed in double.
@@ -57,33 +63,35 @@ typedef struct {
   int q_tile;        /* T (prefill); ignored for decode */
   double scale;      /* logit scale, usually 1/sqrt(d) */
   int dtype;         /* 0 = float32, 1 = bfloat16 bits */
+  int shared_index_set; /* 0: one index set per KV head; 1: one set shared by all heads */
 } oracle_problem;
 
 /* All functions return 0 on success and a negative value on a bad argument.
  * "units" is a flat list of unit coordinates; NULL means every unit in
  * row-major order. nthreads <= 0 means the OpenMP default. */
 
-/* Anchor, decode. Unit = (b, kv): 2 ints each.
+/* Anchor, decode. Unit = (b, s): 2 ints each, s the index set (the KV head,
+ * or 0 for a shared set).
  * idx_out    [nunits][k]   selected key indices, ascending.
- * pooled_out [nunits][N]   mean post-softmax probability over the group (nullable). */
+ * pooled_out [nunits][N]   mean post-softmax probability over the set's heads (nullable). */
 int oracle_anchor_decode(const oracle_problem* p, const void* q, const void* k,
                          const int32_t* units, int nunits,
                          int32_t* idx_out, double* pooled_out, int nthreads);
 
-/* Anchor, causal prefill. Unit = (b, kv, t): 3 ints each.
+/* Anchor, causal prefill. Unit = (b, s, t): 3 ints each.
  * idx_out    [nunits][k]   ascending, -1 after k_t entries.
- * pooled_out [nunits][N]   mean over group heads and tile rows; 0 for j >= prefix_t (nullable). */
+ * pooled_out [nunits][N]   mean over the set's heads and the tile's rows; 0 for j >= prefix_t (nullable). */
 int oracle_anchor_prefill(const oracle_problem* p, const void* q, const void* k,
                           const int32_t* units, int nunits,
                           int32_t* idx_out, double* pooled_out, int nthreads);
 
-/* Reuse, decode. Unit = (b, h): 2 ints. idx is [B, Hkv, 1, k].
+/* Reuse, decode. Unit = (b, h): 2 ints. idx is [B, S, 1, k], S = Hkv or 1 (shared).
  * out [nunits][d]. */
 int oracle_reuse_decode(const oracle_problem* p, const void* q, const void* k, const void* v,
                         const int32_t* idx, const int32_t* units, int nunits,
                         double* out, int nthreads);
 
-/* Reuse, causal prefill. Unit = (b, h, i): 3 ints. idx is [B, Hkv, tiles, k].
+/* Reuse, causal prefill. Unit = (b, h, i): 3 ints. idx is [B, S, tiles, k].
  * out [nunits][d]; a row whose restricted set is empty gets zeros. */
 int oracle_reuse_prefill(const oracle_problem* p, const void* q, const void* k, const void* v,
                          const int32_t* idx, const int32_t* units, int nunits,

@@ -385,4 +385,97 @@ def pin_bf16_same_as_f32_values(orc):
     assert np.array_equal(o1, o2)
 
 
+
+# ---- the non-head-aware variant: one index set shared by every head ---------------
+
+def pin_shared_pooled_vs_sdpa(orc):
+    """Shared sets rank the mean over ALL query heads (and tile rows) of the
+    post-softmax probabilities; every head's probabilities come from its own
+    KV head."""
+    for dtype in (torch.float32, torch.bfloat16):
+        B, Hq, Hkv, d, N, K = 2, 6, 3, 16, 40, 7
+        q = _rand((B, Hq, 1, d), 141, dtype)
+        k = _rand((B, Hkv, N, d), 142, dtype)
+        ref = _probabilities(q, k)[:, :, 0, :].mean(1).numpy()        # [B, N]
+        idx, pooled = orc.anchor_decode(_host(q), _host(k), K, shared=True)
+        assert idx.shape == (B, K)
+        _close(pooled, ref, 1e-13, what=f"shared decode pooled {dtype}")
+        for b in range(B):
+            _check_topk(idx[b], ref[b], K, f"shared decode top-k b{b}")
+        # differs from every per-KV-head ranking on this input
+        per_kv, _ = orc.anchor_decode(_host(q), _host(k), K)
+        assert not any(np.array_equal(idx[0], per_kv[kv]) for kv in range(Hkv))
+    B, Hq, Hkv, d, N, T, K = 1, 4, 2, 8, 37, 8, 11
+    q = _rand((B, Hq, N, d), 143)
+    k = _rand((B, Hkv, N, d), 144)
+    P = _probabilities(q, k, causal=True)[0]                           # [Hq, N, N]
+    tiles = -(-N // T)
+    idx, pooled = orc.anchor_prefill(_host(q), _host(k), K, T, shared=True)
+    assert idx.shape == (tiles, K)
+    for t in range(tiles):
+        r0, r1 = t * T, min((t + 1) * T, N)
+        ref = P[:, r0:r1, :].mean((0, 1)).numpy()
+        _close(pooled[t], ref, 1e-13, what=f"shared prefill pooled t{t}")
+        _check_topk(idx[t], ref[:r1], min(K, r1), f"shared prefill top-k t{t}")
+
+
+def pin_shared_topk_brute_force(orc):
+    """Two KV heads, one shared set: it maximises the all-head mean mass over all k-subsets."""
+    B, Hq, Hkv, d, N, K = 1, 4, 2, 8, 11, 4
+    q = _rand((B, Hq, 1, d), 151)
+    k = _rand((B, Hkv, N, d), 152, scale=2.0)
+    score = _probabilities(q, k).reshape(Hq, N).mean(0).numpy()
+    best = max(itertools.combinations(range(N), K), key=lambda s: sum(score[list(s)]))
+    idx, _ = orc.anchor_decode(_host(q), _host(k), K, shared=True)
+    assert idx[0].tolist() == list(best), (idx[0], best)
+
+
+def pin_shared_reuse_vs_masked_sdpa(orc):
+    """Every head attends through the one set of its batch row (and tile)."""
+    rng = np.random.default_rng(16)
+    B, Hq, Hkv, d, N, K = 2, 6, 3, 16, 50, 9
+    q = _rand((B, Hq, 1, d), 161)
+    k = _rand((B, Hkv, N, d), 162)
+    v = _rand((B, Hkv, N, d), 163)
+    idx = _random_sets(rng, B, N, K).reshape(B, 1, 1, K)
+    mask = torch.zeros((B, Hq, 1, N), dtype=torch.bool)
+    for b in range(B):
+        sel = idx[b, 0, 0]
+        mask[b, :, 0, sel[sel >= 0]] = True
+    out = orc.reuse_decode(_host(q), _host(k), _host(v), idx, shared=True)
+    _close(out, _sdpa(q, k, v, mask=mask).reshape(-1, d), 1e-12, what="shared reuse decode")
+    B, N, T, K = 1, 29, 8, 5
+    tiles = -(-N // T)
+    q = _rand((B, Hq, N, d), 164)
+    k = _rand((B, Hkv, N, d), 165)
+    v = _rand((B, Hkv, N, d), 166)
+    idx = _random_sets(rng, tiles, [min((t + 1) * T, N) for t in range(tiles)], K).reshape(B, 1, tiles, K)
+    mask = torch.zeros((B, Hq, N, N), dtype=torch.bool)
+    for i in range(N):
+        sel = idx[0, 0, i // T]
+        mask[0, :, i, sel[(sel >= 0) & (sel <= i)]] = True
+    out = orc.reuse_prefill(_host(q), _host(k), _host(v), idx, T, shared=True).reshape(Hq, N, d)
+    empty = ~mask[0].any(-1)
+    ref = _sdpa(q, k, v, mask=mask)[0]
+    ref[empty] = 0.0
+    _close(out, ref.numpy(), 1e-12, what="shared reuse prefill")
+
+
+def pin_shared_is_head_aware_with_one_kv_head(orc):
+    """With one KV head the shared set is the head-aware set."""
+    B, Hq, Hkv, d, N, T, K = 2, 4, 1, 16, 33, 8, 6
+    q = _host(_rand((B, Hq, 1, d), 171))
+    k = _host(_rand((B, Hkv, N, d), 172))
+    v = _host(_rand((B, Hkv, N, d), 173))
+    a, pa = orc.anchor_decode(q, k, K)
+    s, ps = orc.anchor_decode(q, k, K, shared=True)
+    assert np.array_equal(a, s) and np.array_equal(pa, ps)
+    ia = a.reshape(B, 1, 1, K)
+    assert np.array_equal(orc.reuse_decode(q, k, v, ia), orc.reuse_decode(q, k, v, ia, shared=True))
+    qp = _host(_rand((B, Hq, N, d), 174))
+    a, pa = orc.anchor_prefill(qp, k, K, T)
+    s, ps = orc.anchor_prefill(qp, k, K, T, shared=True)
+    assert np.array_equal(a, s) and np.array_equal(pa, ps)
+
+
 ALL_PINS = [v for n, v in sorted(globals().items()) if n.startswith("pin_")]

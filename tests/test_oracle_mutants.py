@@ -14,11 +14,23 @@ import oracle_pins  # noqa: E402
 
 MUTANTS = {
     "pool_not_divided_by_G": (
-        "for (int j = 0; j < N; ++j) pooled[j] /= G;",
+        "for (int j = 0; j < N; ++j) pooled[j] /= nh;",
         "for (int j = 0; j < N; ++j) pooled[j] /= 1;"),
     "pool_first_head_only": (
-        "for (int g = 0; g < G; ++g) {\n        int h = kvh * G + g;  /* query heads",
-        "for (int g = 0; g < 1; ++g) {\n        int h = kvh * G + g;  /* query heads"),
+        "*h0 = set * G;\n    *nh = G;",
+        "*h0 = set * G;\n    *nh = 1;"),
+    "shared_pools_one_group": (
+        "*h0 = 0;\n    *nh = p->num_q_heads;",
+        "*h0 = 0;\n    *nh = G;"),
+    "shared_pools_first_kv_for_all_heads": (
+        "s[j] = logit(p, q, k, b, h, 0, h / G, j);",
+        "s[j] = logit(p, q, k, b, h, 0, p->shared_index_set ? 0 : h / G, j);"),
+    "shared_reuse_ignores_batch": (
+        "idx + ((size_t)b * index_sets(p) + set_of_head(p, h)) * K;",
+        "idx + ((size_t)b * (p->shared_index_set ? 0 : index_sets(p)) + set_of_head(p, h)) * K;"),
+    "shared_reuse_prefill_first_tile": (
+        "idx + (((size_t)b * index_sets(p) + set_of_head(p, h)) * tiles + t) * K;",
+        "idx + (((size_t)b * index_sets(p) + set_of_head(p, h)) * tiles + (p->shared_index_set ? 0 : t)) * K;"),
     "gqa_mapping_modulo": (
         "const int kvh = h / (p->num_q_heads / p->num_kv_heads), d = p->head_dim;",
         "const int kvh = h % p->num_kv_heads, d = p->head_dim;"),
@@ -41,8 +53,8 @@ MUTANTS = {
         "out[c] += s[a] * element(v, p->dtype, vo + c);",
         "out[c] += s[a] * element(k, p->dtype, vo + c);"),
     "ragged_tile_divided_by_T": (
-        "pooled[j] /= (double)G * rows;",
-        "pooled[j] /= (double)G * T;"),
+        "pooled[j] /= (double)nh * rows;",
+        "pooled[j] /= (double)nh * T;"),
     "prefill_candidates_past_prefix": (
         "select_top_k(pooled, prefix, p->top_k,",
         "select_top_k(pooled, N, p->top_k,"),
