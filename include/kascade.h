@@ -23,13 +23,21 @@
  *     keys. Causal rows see keys j <= i, the diagonal included.
  *   - Exactly equal scores are ranked lower key index first.
  *   - The saved set is used as is: no extra window, sink or diagonal keys.
+ *   - Non-head-aware variant (shared_index_set = 1), the ablation baseline the
+ *     pages compare head-aware selection against (euno.news summary, "Key
+ *     Contributions" and "Results & Findings"): the ranking score is the mean
+ *     over ALL Hq query heads (each against its own KV head) of the
+ *     post-softmax probabilities, one set per batch row (and prefill tile),
+ *     and every head's reuse attends through that one set. With Hkv = 1 it is
+ *     the head-aware selection.
  *
  * Layouts (all row-major, contiguous, caller-owned device memory):
  *   Q, O : [B, Hq,  q_len,  d]    (decode: q_len = 1)
  *   K, V : [B, Hkv, kv_len, d]    (prefill: q_len == kv_len == N)
- *   idx  : int32 [B, Hkv, tiles, k]; tiles = 1 for decode, ceil(N/T) for
- *          prefill. Entries [0, k_t) are the selected key positions in
- *          ascending order; entries [k_t, k) are -1.
+ *   idx  : int32 [B, S, tiles, k]; S = Hkv, or 1 with shared_index_set;
+ *          tiles = 1 for decode, ceil(N/T) for prefill. Entries [0, k_t) are
+ *          the selected key positions in ascending order; entries [k_t, k)
+ *          are -1.
  *   lse  : float32 [B, Hq, q_len], natural-log sum of exp of the scaled logits
  *          over the keys the row attends to in the anchor (dense) pass.
  * Element type: dtype KASCADE_F32 (float32) or KASCADE_BF16 (bfloat16) for Q,
@@ -87,6 +95,10 @@ typedef struct {
   int32_t q_tile;       /* T (prefill only): 128 */
   float scale;          /* logit scale; <= 0 selects 1/sqrt(d) */
   int32_t dtype;        /* kascade_dtype; prefill requires KASCADE_BF16 */
+  int32_t shared_index_set; /* 0: one index set per KV head (head-aware, the
+                               method); 1: one set per batch row (and tile)
+                               shared by every head, the non-head-aware
+                               ablation. Any other value is invalid. */
 } kascade_problem;
 
 /* Check a problem for an op without touching the GPU. Returns KASCADE_OK,
@@ -101,7 +113,7 @@ size_t kascade_workspace_bytes(const kascade_problem* p, int op);
 
 /* Anchor layer, one decode query per (batch, query head).
  * Computes dense scores of q against all N keys, the per-KV-head pooled
- * post-softmax score, and its exact top-k into idx [B, Hkv, 1, k].
+ * post-softmax score, and its exact top-k into idx [B, S, 1, k].
  * out (nullable): dense attention output [B, Hq, 1, d] (reads V; v may be
  * NULL when out is NULL). lse (nullable): [B, Hq, 1]. */
 int kascade_anchor_decode(const kascade_problem* p, const void* q, const void* k,
@@ -109,7 +121,8 @@ int kascade_anchor_decode(const kascade_problem* p, const void* q, const void* k
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* Reuse layer, decode. For each (b, h): softmax attention of q over the keys
- * idx[b, h/G, 0, :] with this layer's K and V, written to out [B, Hq, 1, d].
+ * idx[b, h/G, 0, :] (idx[b, 0, 0, :] with a shared set) with this layer's K
+ * and V, written to out [B, Hq, 1, d].
  * Entries -1 (and any entry outside [0, N)) are skipped; a row whose list has
  * no usable entry gets zeros. */
 int kascade_reuse_decode(const kascade_problem* p, const void* q, const void* k,
@@ -118,15 +131,15 @@ int kascade_reuse_decode(const kascade_problem* p, const void* q, const void* k,
 
 /* Anchor layer, causal prefill. For each (b, KV head, query tile t): the mean
  * over the tile's rows and the group's heads of the causal post-softmax
- * probabilities, and its exact top-k_t among keys < prefix_t into
- * idx [B, Hkv, ceil(N/T), k]. out (nullable): dense causal attention output
+ * probabilities (all heads' with a shared set), and its exact top-k_t among
+ * keys < prefix_t into idx [B, S, ceil(N/T), k]. out (nullable): dense causal attention output
  * [B, Hq, N, d]. lse (nullable): [B, Hq, N]. */
 int kascade_anchor_prefill(const kascade_problem* p, const void* q, const void* k,
                            const void* v, void* out, int32_t* idx, float* lse,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* Reuse layer, causal prefill. Row i of tile t attends to the keys
- * j in idx[b, h/G, t, 0:k_t] with 0 <= j <= i (entries -1, or outside the
+ * j in idx[b, h/G, t, 0:k_t] (set 0 when shared) with 0 <= j <= i (entries -1, or outside the
  * sequence, are skipped); a row with no such key gets zeros. Output
  * out [B, Hq, N, d]. Slots at or past k_t = min(k, prefix_t) are not read. */
 int kascade_reuse_prefill(const kascade_problem* p, const void* q, const void* k,

@@ -66,7 +66,8 @@ __global__ __launch_bounds__(256) void decode_attn_bf16(DecodeArgs a) {
   const u16* q = static_cast<const u16*>(a.q);
   const u16* kb = static_cast<const u16*>(a.k) + (size_t)(b * a.hkv + kvh) * a.n * D;
   const u16* vb = static_cast<const u16*>(a.v) + (size_t)(b * a.hkv + kvh) * a.n * D;
-  const int32_t* list = GATHER ? a.idx + (size_t)(b * a.hkv + kvh) * a.list_len : nullptr;
+  const int32_t* list =
+      GATHER ? a.idx + (size_t)(b * a.idx_sets + (a.idx_sets == 1 ? 0 : kvh)) * a.list_len : nullptr;
 
   // B operand: query head n of the group, d = 32c + 8qg + s; padded heads are 0.
   bf16x8 bq[C];
@@ -276,7 +277,8 @@ __global__ __launch_bounds__(256) void decode_attn_f32(DecodeArgs a) {
   if (split >= a.splits) return;
   const float* kb = static_cast<const float*>(a.k) + (size_t)(b * a.hkv + kvh) * a.n * D;
   const float* vb = static_cast<const float*>(a.v) + (size_t)(b * a.hkv + kvh) * a.n * D;
-  const int32_t* list = GATHER ? a.idx + (size_t)(b * a.hkv + kvh) * a.list_len : nullptr;
+  const int32_t* list =
+      GATHER ? a.idx + (size_t)(b * a.idx_sets + (a.idx_sets == 1 ? 0 : kvh)) * a.list_len : nullptr;
   const int begin = split * a.keys_per_split;
   const int end = min(begin + a.keys_per_split, a.list_len);
 

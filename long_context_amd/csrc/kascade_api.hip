@@ -39,6 +39,7 @@ int validate(const kascade_problem* p, int op) {
     return KASCADE_ERR_INVALID;
   if (p->num_q_heads % p->num_kv_heads != 0) return KASCADE_ERR_INVALID;
   if (p->dtype != KASCADE_F32 && p->dtype != KASCADE_BF16) return KASCADE_ERR_INVALID;
+  if (p->shared_index_set != 0 && p->shared_index_set != 1) return KASCADE_ERR_INVALID;
   // NaN scale, tested on the bit pattern (the library is built assuming no NaN
   // operands, so a floating-point comparison could be folded away).
   uint32_t scale_bits;
@@ -49,6 +50,7 @@ int validate(const kascade_problem* p, int op) {
       (long long)p->batch * p->num_kv_heads * p->kv_len >= (1ll << 31))
     return KASCADE_ERR_UNSUPPORTED;
   if (p->head_dim != 64 && p->head_dim != 128) return KASCADE_ERR_UNSUPPORTED;
+  if (p->batch > 65535) return KASCADE_ERR_UNSUPPORTED;  // a grid dimension in places
   if (p->num_q_heads / p->num_kv_heads > kMaxGroup) return KASCADE_ERR_UNSUPPORTED;
   if (is_decode(op)) {
     if (p->q_len != 1) return KASCADE_ERR_INVALID;
@@ -108,7 +110,7 @@ DecodeWorkspace decode_workspace(const kascade_problem* p, int op) {
 }
 
 struct PrefillWorkspace {
-  size_t lse2, pooled, total;
+  size_t lse2, pooled, shared, total;
 };
 
 PrefillWorkspace prefill_workspace(const kascade_problem* p, int op) {
@@ -120,6 +122,10 @@ PrefillWorkspace prefill_workspace(const kascade_problem* p, int op) {
     w.pooled = off;
     off += align_up((size_t)p->batch * p->num_kv_heads * prefill_ragged_len(p->kv_len, p->q_tile) *
                     sizeof(float));
+    if (p->shared_index_set) {
+      w.shared = off;
+      off += align_up((size_t)p->batch * prefill_ragged_len(p->kv_len, p->q_tile) * sizeof(float));
+    }
     w.total = off;
   }
   return w;
@@ -208,6 +214,7 @@ DecodeArgs decode_args(const kascade_problem* p, const void* q, const void* k, c
   a.k = k;
   a.v = v;
   a.idx = idx;
+  a.idx_sets = p->shared_index_set ? 1 : p->num_kv_heads;
   a.batch = p->batch;
   a.hq = p->num_q_heads;
   a.hkv = p->num_kv_heads;
@@ -231,6 +238,7 @@ PrefillArgs prefill_args(const kascade_problem* p, const void* q, const void* k,
   a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v);
   a.idx = idx;
+  a.idx_sets = p->shared_index_set ? 1 : p->num_kv_heads;
   a.batch = p->batch;
   a.hq = p->num_q_heads;
   a.hkv = p->num_kv_heads;
@@ -287,8 +295,14 @@ int kascade_anchor_decode(const kascade_problem* p, const void* q, const void* k
   KASCADE_TRY("decode_attn_dense", launch_decode_attn(a, bf16, false, out != nullptr, s));
   KASCADE_TRY("decode_combine", launch_decode_combine(a.part_ml, a.part_o, p->batch * a.hq,
                                                       a.splits, a.d, bf16, out, lse, lse2, s));
-  KASCADE_TRY("topk_decode", launch_topk_decode(a.logits, a.logits_ld, lse2, p->batch, a.hq, a.hkv,
-                                                a.group, a.n, p->top_k, pooled, idx, s));
+  if (p->shared_index_set) {
+    KASCADE_TRY("pool_all_heads", launch_pool_all_heads(a.logits, a.logits_ld, lse2, p->batch, a.hq,
+                                                        a.n, pooled, s));
+    KASCADE_TRY("topk_rows", launch_topk_rows(pooled, p->batch, a.n, p->top_k, idx, s));
+  } else {
+    KASCADE_TRY("topk_decode", launch_topk_decode(a.logits, a.logits_ld, lse2, p->batch, a.hq, a.hkv,
+                                                  a.group, a.n, p->top_k, pooled, idx, s));
+  }
   return KASCADE_OK;
 }
 
@@ -333,7 +347,15 @@ int kascade_anchor_prefill(const kascade_problem* p, const void* q, const void* 
   a.pooled = reinterpret_cast<float*>(ws + w.pooled);
   KASCADE_TRY("prefill_dense", launch_prefill_dense(a, s));
   KASCADE_TRY("prefill_pool", launch_prefill_pool(a, s));
-  KASCADE_TRY("topk_prefill", launch_topk_prefill(a.pooled, p->batch, a.hkv, a.n, a.tile, p->top_k, idx, s));
+  if (p->shared_index_set) {
+    float* shared = reinterpret_cast<float*>(ws + w.shared);
+    KASCADE_TRY("sum_sets", launch_sum_sets(a.pooled, p->batch, a.hkv,
+                                            prefill_ragged_len(a.n, a.tile), shared, s));
+    KASCADE_TRY("topk_prefill", launch_topk_prefill(shared, p->batch, 1, a.n, a.tile, p->top_k, idx, s));
+  } else {
+    KASCADE_TRY("topk_prefill", launch_topk_prefill(a.pooled, p->batch, a.hkv, a.n, a.tile, p->top_k,
+                                                    idx, s));
+  }
   if (lse)
     KASCADE_TRY("lse_convert", launch_lse2_to_lse(a.lse2, lse, (size_t)p->batch * a.hq * a.n, s));
   return KASCADE_OK;

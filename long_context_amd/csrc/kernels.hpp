@@ -16,7 +16,8 @@ struct DecodeArgs {
   const void* q;         // [B, Hq, 1, d]
   const void* k;         // [B, Hkv, N, d]
   const void* v;         // [B, Hkv, N, d] (only read when with_pv)
-  const int32_t* idx;    // gather mode: [B, Hkv, 1, list_len]
+  const int32_t* idx;    // gather mode: [B, idx_sets, 1, list_len]
+  int idx_sets;          // Hkv (a set per KV head) or 1 (one set for all heads)
   int batch, hq, hkv, group, n, list_len, d;
   int keys_per_split, splits;
   float scale_log2;      // logit scale times log2(e)
@@ -46,6 +47,17 @@ hipError_t launch_decode_combine(const float* part_ml, const float* part_o, int 
 hipError_t launch_topk_decode(const float* logits, int ld, const float* lse2, int batch, int hq,
                               int hkv, int group, int n, int k, float* spill, int32_t* idx,
                               hipStream_t s);
+// Rows of n scores each, one selection per row: [rows, n] -> idx [rows, k].
+hipError_t launch_topk_rows(const float* scores, int rows, int n, int k, int32_t* idx,
+                            hipStream_t s);
+// Decode, one set for all heads: pooled[b][j] = sum over the Hq heads of
+// exp2(logit - lse2) from the logits [B*Hq, ld] and lse2 [B*Hq].
+hipError_t launch_pool_all_heads(const float* logits, int ld, const float* lse2, int batch, int hq,
+                                 int n, float* pooled, hipStream_t s);
+// Prefill, one set for all heads: out[b][e] = sum over the Hkv ragged rows of
+// batch b of pooled[(b*Hkv + kv)*len + e].
+hipError_t launch_sum_sets(const float* pooled, int batch, int hkv, size_t len, float* out,
+                           hipStream_t s);
 // Prefill: segment (b, kv, t) covers prefix_t = min((t+1)*T, N) scores stored
 // ragged: base (b*Hkv + kv) * ragged_len + T*t*(t+1)/2.
 hipError_t launch_topk_prefill(const float* scores, int batch, int hkv, int n, int tile, int k,
@@ -65,7 +77,8 @@ struct PrefillArgs {
   const uint16_t* q;     // [B, Hq, N, d] bf16
   const uint16_t* k;     // [B, Hkv, N, d]
   const uint16_t* v;
-  const int32_t* idx;    // reuse: [B, Hkv, tiles, topk]
+  const int32_t* idx;    // reuse: [B, idx_sets, tiles, topk]
+  int idx_sets;          // Hkv (a set per KV head) or 1 (one set for all heads)
   int batch, hq, hkv, group, n, d, tile, tiles, topk;
   float scale_log2;
   uint16_t* out;         // [B, Hq, N, d] bf16 (optional in the anchor)

@@ -108,7 +108,8 @@ __global__ __launch_bounds__(256 * NH) void prefill_attn(PrefillArgs a) {
 
   const u16* kb = a.k + (size_t)(b * a.hkv + kvh) * a.n * D;
   const u16* vb = a.v + (size_t)(b * a.hkv + kvh) * a.n * D;
-  const int32_t* list = GATHER ? a.idx + ((size_t)(b * a.hkv + kvh) * a.tiles + t) * a.topk : nullptr;
+  const int set = a.idx_sets == 1 ? 0 : kvh;
+  const int32_t* list = GATHER ? a.idx + ((size_t)(b * a.idx_sets + set) * a.tiles + t) * a.topk : nullptr;
   const int list_len = GATHER ? min(a.topk, prefix) : prefix;
   const int nchunks = (list_len + kKeyChunk - 1) / kKeyChunk;
 

@@ -22,6 +22,11 @@
 // Decode fuses the pooling: the segment of KV head kv is produced here from
 // the group's scaled logits and row log-sum-exps, sum over heads of
 // exp2(logit - lse2), straight into registers.
+//
+// One set shared by all heads (the non-head-aware ablation) pools first, in a
+// separate pass: decode sums exp2(logit - lse2) over all Hq heads per key;
+// prefill sums the per-KV-head pooled rows of a batch row. The selection then
+// runs on those rows. Sums rank keys as the means do.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -322,7 +327,61 @@ __global__ __launch_bounds__(kThreads) void topk_prefill_kernel(const float* poo
   }
 }
 
+constexpr int kPoolThreads = 256;
+
+// pooled[b][j] = sum over the hq heads of batch row b of exp2(logit - lse2);
+// one thread per key, heads walked in order, loads coalesced over keys.
+__global__ __launch_bounds__(kPoolThreads) void pool_all_heads_kernel(const float* logits, int ld,
+                                                                        const float* lse2, int hq,
+                                                                        int n, float* pooled) {
+  const int b = blockIdx.y;
+  const int j = blockIdx.x * kPoolThreads + threadIdx.x;
+  if (j >= n) return;
+  const float* lg = logits + (size_t)b * hq * ld + j;
+  const float* l2 = lse2 + (size_t)b * hq;
+  float acc = 0.f;
+  for (int h = 0; h < hq; ++h) acc += fast_exp2(lg[(size_t)h * ld] - l2[h]);
+  pooled[(size_t)b * n + j] = acc;
+}
+
+// out[b][e] = sum over kv of pooled[(b*hkv + kv)*len + e].
+__global__ __launch_bounds__(kPoolThreads) void sum_sets_kernel(const float* pooled, int hkv,
+                                                                  size_t len, float* out) {
+  const int b = blockIdx.y;
+  const float* src = pooled + (size_t)b * hkv * len;
+  for (size_t e = (size_t)blockIdx.x * kPoolThreads + threadIdx.x; e < len;
+       e += (size_t)gridDim.x * kPoolThreads) {
+    float acc = 0.f;
+    for (int kv = 0; kv < hkv; ++kv) acc += src[(size_t)kv * len + e];
+    out[(size_t)b * len + e] = acc;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_topk_rows(const float* scores, int rows, int n, int k, int32_t* idx,
+                            hipStream_t s) {
+  // A row is a single prefill segment whose tile spans all n keys.
+  hipLaunchKernelGGL(topk_prefill_kernel, dim3(1, 1, rows), dim3(kThreads), 0, s, scores, 1, n, n, 1,
+                     (size_t)n, k, idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_pool_all_heads(const float* logits, int ld, const float* lse2, int batch, int hq,
+                                 int n, float* pooled, hipStream_t s) {
+  hipLaunchKernelGGL(pool_all_heads_kernel, dim3((n + kPoolThreads - 1) / kPoolThreads, batch),
+                     dim3(kPoolThreads), 0, s, logits, ld, lse2, hq, n, pooled);
+  return hipGetLastError();
+}
+
+hipError_t launch_sum_sets(const float* pooled, int batch, int hkv, size_t len, float* out,
+                           hipStream_t s) {
+  const size_t want = (len + kPoolThreads - 1) / kPoolThreads;
+  const int blocks = (int)(want < 1024 ? want : 1024);
+  hipLaunchKernelGGL(sum_sets_kernel, dim3(blocks, batch), dim3(kPoolThreads), 0, s, pooled, hkv, len,
+                     out);
+  return hipGetLastError();
+}
 
 hipError_t launch_topk_decode(const float* logits, int ld, const float* lse2, int batch, int hq,
                               int hkv, int group, int n, int k, float* spill, int32_t* idx,

@@ -38,6 +38,7 @@ class Problem(ctypes.Structure):
         ("q_tile", ctypes.c_int32),
         ("scale", ctypes.c_float),
         ("dtype", ctypes.c_int32),
+        ("shared_index_set", ctypes.c_int32),
     ]
 
 
@@ -138,13 +139,28 @@ def _dtype_code(t):
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
-def problem(q, k, top_k, q_tile=128, scale=0.0):
-    """Problem descriptor from Q [B,Hq,L,d] and K [B,Hkv,N,d]."""
+def problem(q, k, top_k, q_tile=128, scale=0.0, shared=False):
+    """Problem descriptor from Q [B,Hq,L,d] and K [B,Hkv,N,d]; shared=True asks
+    for one index set shared by all heads instead of one per KV head."""
     B, Hq, L, d = q.shape
     Bk, Hkv, N, dk = k.shape
     if Bk != B or dk != d:
         raise ValueError(f"shape mismatch q {tuple(q.shape)} k {tuple(k.shape)}")
-    return Problem(B, Hq, Hkv, d, L, N, int(top_k), int(q_tile), float(scale), _dtype_code(q))
+    return Problem(B, Hq, Hkv, d, L, N, int(top_k), int(q_tile), float(scale), _dtype_code(q),
+                   int(bool(shared)))
+
+
+def idx_shape(prob):
+    """Shape of the index sets for a problem: [B, S, tiles, k], S = Hkv or 1 (shared)."""
+    sets = 1 if prob.shared_index_set else prob.num_kv_heads
+    tiles = 1 if prob.q_len == 1 else -(-prob.kv_len // max(prob.q_tile, 1))
+    return (prob.batch, sets, tiles, prob.top_k)
+
+
+def _check_idx(idx, prob, what):
+    want = idx_shape(prob)
+    if tuple(idx.shape) != want or idx.dtype != torch.int32:
+        raise ValueError(f"{what}: idx must be int32 {list(want)}, got {idx.dtype} {list(idx.shape)}")
 
 
 def _ptr(t):
@@ -171,13 +187,15 @@ def _ws(ws):
     return (None, 0) if ws is None else (ws.data_ptr(), ws.numel())
 
 
-def anchor_decode(q, k, v, top_k, out=None, lse=None, idx=None, ws=None, scale=0.0, stream=None):
-    """Anchor decode; returns idx [B,Hkv,1,k] int32 (and fills out/lse if given)."""
+def anchor_decode(q, k, v, top_k, out=None, lse=None, idx=None, ws=None, scale=0.0, stream=None,
+                  shared=False):
+    """Anchor decode; returns idx [B,S,1,k] int32, S = Hkv or 1 with shared=True
+    (and fills out/lse if given)."""
     lib = library()
-    prob = problem(q, k, top_k, 1, scale)
-    B, Hkv = k.shape[0], k.shape[1]
+    prob = problem(q, k, top_k, 1, scale, shared)
     if idx is None:
-        idx = torch.empty((B, Hkv, 1, top_k), dtype=torch.int32, device=q.device)
+        idx = torch.empty(idx_shape(prob), dtype=torch.int32, device=q.device)
+    _check_idx(idx, prob, "anchor_decode")
     if ws is None:
         ws = workspace(prob, OP_ANCHOR_DECODE, q.device)
     wp, wb = _ws(ws)
@@ -186,10 +204,11 @@ def anchor_decode(q, k, v, top_k, out=None, lse=None, idx=None, ws=None, scale=0
     return idx
 
 
-def reuse_decode(q, k, v, idx, out=None, ws=None, scale=0.0, stream=None):
-    """Reuse decode over idx [B,Hkv,1,k]; returns out [B,Hq,1,d]."""
+def reuse_decode(q, k, v, idx, out=None, ws=None, scale=0.0, stream=None, shared=False):
+    """Reuse decode over idx [B,S,1,k] (S = Hkv, or 1 with shared=True); returns out [B,Hq,1,d]."""
     lib = library()
-    prob = problem(q, k, idx.shape[-1], 1, scale)
+    prob = problem(q, k, idx.shape[-1], 1, scale, shared)
+    _check_idx(idx, prob, "reuse_decode")
     if out is None:
         out = torch.empty_like(q)
     if ws is None:
@@ -201,13 +220,13 @@ def reuse_decode(q, k, v, idx, out=None, ws=None, scale=0.0, stream=None):
 
 
 def anchor_prefill(q, k, v, top_k, q_tile=128, out=None, lse=None, idx=None, ws=None, scale=0.0,
-                   stream=None):
-    """Anchor causal prefill; returns idx [B,Hkv,ceil(N/T),k] int32."""
+                   stream=None, shared=False):
+    """Anchor causal prefill; returns idx [B,S,ceil(N/T),k] int32, S = Hkv or 1 with shared=True."""
     lib = library()
-    prob = problem(q, k, top_k, q_tile, scale)
-    B, Hkv, N = k.shape[0], k.shape[1], k.shape[2]
+    prob = problem(q, k, top_k, q_tile, scale, shared)
     if idx is None:
-        idx = torch.empty((B, Hkv, -(-N // q_tile), top_k), dtype=torch.int32, device=q.device)
+        idx = torch.empty(idx_shape(prob), dtype=torch.int32, device=q.device)
+    _check_idx(idx, prob, "anchor_prefill")
     if ws is None:
         ws = workspace(prob, OP_ANCHOR_PREFILL, q.device)
     wp, wb = _ws(ws)
@@ -216,10 +235,12 @@ def anchor_prefill(q, k, v, top_k, q_tile=128, out=None, lse=None, idx=None, ws=
     return idx
 
 
-def reuse_prefill(q, k, v, idx, q_tile=128, out=None, ws=None, scale=0.0, stream=None):
-    """Reuse causal prefill over idx [B,Hkv,tiles,k]; returns out [B,Hq,N,d]."""
+def reuse_prefill(q, k, v, idx, q_tile=128, out=None, ws=None, scale=0.0, stream=None, shared=False):
+    """Reuse causal prefill over idx [B,S,tiles,k] (S = Hkv, or 1 with shared=True);
+    returns out [B,Hq,N,d]."""
     lib = library()
-    prob = problem(q, k, idx.shape[-1], q_tile, scale)
+    prob = problem(q, k, idx.shape[-1], q_tile, scale, shared)
+    _check_idx(idx, prob, "reuse_prefill")
     if out is None:
         out = torch.empty_like(q)
     if ws is None:
@@ -255,14 +276,16 @@ def anchor_schedule(n_layers, anchors):
     return roles
 
 
-def kascade_attention(qs, ks, vs, top_k, anchors, q_tile=128, outs=None, scale=0.0, stream=None):
+def kascade_attention(qs, ks, vs, top_k, anchors, q_tile=128, outs=None, scale=0.0, stream=None,
+                      shared=False):
     """Kascade attention over a stack of layers, one call per layer through the
     C ABI. qs, ks, vs: per-layer tensors, decode (Q [B,Hq,1,d]) or causal
     prefill (Q [B,Hq,N,d]), K/V [B,Hkv,N,d]. Layers before the first anchor
     attend densely (the anchor call's dense output; its indices are not kept),
     an anchor layer outputs dense attention and saves its top-k indices, every
     other layer attends only to the saved indices of the nearest preceding
-    anchor, with its own Q, K and V. Returns (per-layer outputs,
+    anchor, with its own Q, K and V. shared=True runs the non-head-aware
+    ablation (one index set for all heads). Returns (per-layer outputs,
     {anchor layer: idx})."""
     n_layers = len(qs)
     if not (len(ks) == len(vs) == n_layers):
@@ -279,19 +302,23 @@ def kascade_attention(qs, ks, vs, top_k, anchors, q_tile=128, outs=None, scale=0
             kk = min(top_k, n) if (decode or role == "dense") else top_k
             if decode:
                 if ws_anchor is None:
-                    ws_anchor = workspace(problem(q, k, kk, 1, scale), OP_ANCHOR_DECODE, q.device)
-                idx = anchor_decode(q, k, v, kk, out=outs[l], ws=ws_anchor, scale=scale, stream=stream)
+                    ws_anchor = workspace(problem(q, k, kk, 1, scale, shared), OP_ANCHOR_DECODE, q.device)
+                idx = anchor_decode(q, k, v, kk, out=outs[l], ws=ws_anchor, scale=scale, stream=stream,
+                                    shared=shared)
             else:
                 if ws_anchor is None:
-                    ws_anchor = workspace(problem(q, k, kk, q_tile, scale), OP_ANCHOR_PREFILL, q.device)
+                    ws_anchor = workspace(problem(q, k, kk, q_tile, scale, shared), OP_ANCHOR_PREFILL,
+                                          q.device)
                 idx = anchor_prefill(q, k, v, kk, q_tile, out=outs[l], ws=ws_anchor, scale=scale,
-                                     stream=stream)
+                                     stream=stream, shared=shared)
             if role == "anchor":
                 saved[l] = idx
         elif decode:
             if ws_reuse is None:
-                ws_reuse = workspace(problem(q, k, top_k, 1, scale), OP_REUSE_DECODE, q.device)
-            reuse_decode(q, k, v, saved[src], out=outs[l], ws=ws_reuse, scale=scale, stream=stream)
+                ws_reuse = workspace(problem(q, k, top_k, 1, scale, shared), OP_REUSE_DECODE, q.device)
+            reuse_decode(q, k, v, saved[src], out=outs[l], ws=ws_reuse, scale=scale, stream=stream,
+                         shared=shared)
         else:
-            reuse_prefill(q, k, v, saved[src], q_tile, out=outs[l], scale=scale, stream=stream)
+            reuse_prefill(q, k, v, saved[src], q_tile, out=outs[l], scale=scale, stream=stream,
+                          shared=shared)
     return outs, saved

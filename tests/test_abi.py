@@ -132,3 +132,40 @@ def test_entry_points_reject_before_launch(L):
     assert L.anchor_prefill_raw(pp, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, ws_ap - 256, None) == K.ERR_WORKSPACE
     assert L.reuse_prefill_raw(pp, FAKE, FAKE, None, FAKE, FAKE, None, 0, None) == K.ERR_INVALID
     assert L.reuse_prefill_raw(_prefill(dtype=K.F32), FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == K.ERR_UNSUPPORTED
+
+
+def test_shared_index_set_flag(L):
+    """One index set for all heads: 0 and 1 are the only valid values; the
+    prefill anchor needs room for the summed rows, decode needs nothing more."""
+    for op in range(4):
+        mk = _prob if op in (K.OP_ANCHOR_DECODE, K.OP_REUSE_DECODE) else _prefill
+        assert L.validate(mk(shared_index_set=1), op) == K.OK
+        assert L.validate(mk(shared_index_set=2), op) == K.ERR_INVALID
+        assert L.validate(mk(shared_index_set=-1), op) == K.ERR_INVALID
+    assert L.workspace_bytes(_prob(shared_index_set=1), K.OP_ANCHOR_DECODE) == \
+        L.workspace_bytes(_prob(), K.OP_ANCHOR_DECODE)
+    ragged = 128 * 7 * 8 // 2 + 1000           # 8 tiles of 128 over N = 1000
+    grow = L.workspace_bytes(_prefill(shared_index_set=1), K.OP_ANCHOR_PREFILL) - \
+        L.workspace_bytes(_prefill(), K.OP_ANCHOR_PREFILL)
+    assert grow >= 2 * ragged * 4 and grow < 2 * ragged * 4 + 256
+    assert L.validate(_prob(batch=65536, num_q_heads=1, num_kv_heads=1, kv_len=16, top_k=4),
+                      K.OP_ANCHOR_DECODE) == K.ERR_UNSUPPORTED
+
+
+def test_binding_checks_index_set_shape():
+    """The binding refuses an idx whose shape does not match the problem
+    before any call reaches the library (host tensors: nothing is launched)."""
+    import torch
+    q = torch.zeros((2, 8, 1, 128), dtype=torch.bfloat16)
+    k = torch.zeros((2, 2, 300, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="idx must be int32"):
+        K.reuse_decode(q, k, k, torch.zeros((2, 1, 1, 16), dtype=torch.int32))            # per-KV-head expected
+    with pytest.raises(ValueError, match="idx must be int32"):
+        K.reuse_decode(q, k, k, torch.zeros((2, 2, 1, 16), dtype=torch.int32), shared=True)
+    with pytest.raises(ValueError, match="idx must be int32"):
+        K.reuse_decode(q, k, k, torch.zeros((2, 2, 1, 16), dtype=torch.int64))
+    qp = torch.zeros((1, 8, 300, 128), dtype=torch.bfloat16)
+    kp = torch.zeros((1, 2, 300, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="idx must be int32"):
+        K.reuse_prefill(qp, kp, kp, torch.zeros((1, 2, 2, 16), dtype=torch.int32))         # 3 tiles expected
+    assert K.idx_shape(K.problem(qp, kp, 16, 128, shared=True)) == (1, 1, 3, 16)
