@@ -283,7 +283,9 @@ def pooled_prefill(q, k, tile):
 
 def captured_mass(pooled, idx):
     """Mean over index sets of the pooled attention mass the set holds
-    (entries -1 hold none). pooled [..., N], idx [..., k] with equal leading dims."""
+    (entries -1 hold none). pooled [..., N], idx [..., k]; a shared set
+    (idx [B, 1, ...]) is scored against every KV head's pooled row."""
+    idx = idx.expand(*pooled.shape[:-1], idx.shape[-1])
     take = pooled.gather(-1, idx.long().clamp_min(0)) * (idx >= 0)
     return float(take.sum(-1).mean())
 
@@ -291,14 +293,16 @@ def captured_mass(pooled, idx):
 def planted_recall(positions, idx, tile, n):
     """Mean over (b, KV head, tile) of the fraction of planted keys inside the
     tile's causal prefix that the index set holds. positions[b][kv] are one
-    layer's planted rows; idx [B, Hkv, tiles, k] on the host."""
+    layer's planted rows; idx [B, S, tiles, k] on the host, S = Hkv or 1 (a
+    set shared by all heads)."""
     fr = []
     for b, per_kv in enumerate(positions):
         for kv, pos in enumerate(per_kv):
+            s = kv if idx.shape[1] > 1 else 0
             for t in range(idx.shape[2]):
                 live = pos[pos < min((t + 1) * tile, n)] if idx.shape[2] > 1 else pos
                 if live.size:
-                    fr.append(np.isin(live, idx[b, kv, t]).mean())
+                    fr.append(np.isin(live, idx[b, s, t]).mean())
     return float(np.mean(fr))
 
 
@@ -308,12 +312,14 @@ def rel_error(out, ref):
     return float(torch.linalg.vector_norm(o - r) / torch.linalg.vector_norm(r))
 
 
-def accuracy_sweep(w, fractions=SWEEP_K_FRACTIONS, dev="cuda"):
+def accuracy_sweep(w, fractions=SWEEP_K_FRACTIONS, dev="cuda", shared=(False, True)):
     """For each k = N/f: the anchor (layer 0) selects its index sets once, then
     every layer of the stack (the anchor itself included) attends through the
     reuse call to those sets with its own Q, K and V. Per layer: planted-key
     recall, captured pooled attention mass, and the output's error relative to
-    the layer's dense attention. Returns one dict per k."""
+    the layer's dense attention. With shared=(False, True) both head-aware sets
+    ("layers") and one set shared by all heads ("shared_set_layers", the
+    ablation) are measured. Returns one dict per k."""
     decode = w.phase == "decode"
     pos = synth.planted_positions(w)
     layers = [synth.make_layer(w, l, dev, pos) for l in range(w.layers)]
@@ -331,26 +337,29 @@ def accuracy_sweep(w, fractions=SWEEP_K_FRACTIONS, dev="cuda"):
     q0, k0, v0 = layers[0]
     for f in fractions:
         kk = max(1, w.n // f)
-        if decode:
-            idx = K.anchor_decode(q0, k0, v0, kk)
-        else:
-            idx = K.anchor_prefill(q0, k0, v0, kk, w.tile)
-        idx_host = idx.cpu().numpy()
-        per_layer = []
-        for l, (q, k, v) in enumerate(layers):
+        row = {"sweep": "accuracy_vs_k", "workload": w.name, "phase": w.phase, "n": w.n,
+               "q_tile": w.tile if not decode else None, "top_k": kk, "k_over_n": f"1/{f}",
+               "share": w.share, "gain": w.gain}
+        for sh in shared:
             if decode:
-                o = K.reuse_decode(q, k, v, idx)
+                idx = K.anchor_decode(q0, k0, v0, kk, shared=sh)
             else:
-                o = K.reuse_prefill(q, k, v, idx, w.tile)
-            per_layer.append({
-                "layer": l,
-                "planted_recall": round(planted_recall(pos[l], idx_host, w.tile, w.n), 4),
-                "attention_mass": round(captured_mass(pooled[l], idx), 4),
-                "rel_error_vs_dense": round(rel_error(o, dense[l]), 5),
-            })
-        rows.append({"sweep": "accuracy_vs_k", "workload": w.name, "phase": w.phase, "n": w.n,
-                     "q_tile": w.tile if not decode else None, "top_k": kk, "k_over_n": f"1/{f}",
-                     "share": w.share, "gain": w.gain, "layers": per_layer})
+                idx = K.anchor_prefill(q0, k0, v0, kk, w.tile, shared=sh)
+            idx_host = idx.cpu().numpy()
+            per_layer = []
+            for l, (q, k, v) in enumerate(layers):
+                if decode:
+                    o = K.reuse_decode(q, k, v, idx, shared=sh)
+                else:
+                    o = K.reuse_prefill(q, k, v, idx, w.tile, shared=sh)
+                per_layer.append({
+                    "layer": l,
+                    "planted_recall": round(planted_recall(pos[l], idx_host, w.tile, w.n), 4),
+                    "attention_mass": round(captured_mass(pooled[l], idx), 4),
+                    "rel_error_vs_dense": round(rel_error(o, dense[l]), 5),
+                })
+            row["shared_set_layers" if sh else "layers"] = per_layer
+        rows.append(row)
     torch.cuda.synchronize()
     return rows
 

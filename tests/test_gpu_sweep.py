@@ -29,22 +29,28 @@ def test_accuracy_sweep_properties(lib, case):
     fractions = (64, 16, 4, 1)
     log(f"[sweep] {case} N={w.n} fractions={fractions}")
     rows = bench.accuracy_sweep(w, fractions)
+    assert all("shared_set_layers" in r for r in rows)
     assert [r["top_k"] for r in rows] == [max(1, w.n // f) for f in fractions]
     for r in rows:
         log(f"[sweep] {case} k={r['top_k']} " + " ".join(
             f"L{x['layer']}:rec={x['planted_recall']},mass={x['attention_mass']},err={x['rel_error_vs_dense']}"
             for x in r["layers"]))
-    for l in range(w.layers):
-        mass = [r["layers"][l]["attention_mass"] for r in rows]
-        recall = [r["layers"][l]["planted_recall"] for r in rows]
-        # nested index sets: captured mass and planted recall never fall as k grows
-        assert all(b >= a - 1e-4 for a, b in zip(mass, mass[1:])), (l, mass)
-        assert all(b >= a for a, b in zip(recall, recall[1:])), (l, recall)
-        full = rows[-1]["layers"][l]
-        # k = N: every key of every prefix is selected, so reuse is dense attention
-        assert full["attention_mass"] == pytest.approx(1.0, abs=1e-4)
-        assert full["planted_recall"] == 1.0
-        assert full["rel_error_vs_dense"] < 1e-2
+    for key in ("layers", "shared_set_layers"):
+        for l in range(w.layers):
+            mass = [r[key][l]["attention_mass"] for r in rows]
+            recall = [r[key][l]["planted_recall"] for r in rows]
+            # nested index sets: captured mass and planted recall never fall as k grows
+            assert all(b >= a - 1e-4 for a, b in zip(mass, mass[1:])), (key, l, mass)
+            assert all(b >= a for a, b in zip(recall, recall[1:])), (key, l, recall)
+            full = rows[-1][key][l]
+            # k = N: every key of every prefix is selected, so reuse is dense attention
+            assert full["attention_mass"] == pytest.approx(1.0, abs=1e-4)
+            assert full["planted_recall"] == 1.0
+            assert full["rel_error_vs_dense"] < 1e-2
+    # per KV head, its own top-k holds at least as much of the anchor layer's
+    # pooled attention as the shared set of the same size does
+    for r in rows:
+        assert r["layers"][0]["attention_mass"] >= r["shared_set_layers"][0]["attention_mass"] - 2e-3
     # the anchor's sets are its exact top-k: no other set of k keys per segment
     # holds more of the anchor layer's own pooled attention
     q, k, _ = synth.make_layer(w, 0, "cuda")

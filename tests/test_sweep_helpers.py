@@ -74,3 +74,12 @@ def test_rel_error():
     a = torch.tensor([3.0, 4.0])
     assert bench.rel_error(a, a) == 0.0
     assert bench.rel_error(torch.tensor([3.0, 5.0]), a) == pytest.approx(0.2)
+
+
+def test_measures_of_a_shared_set():
+    """A set shared by all KV heads is scored against each head's own rows."""
+    pooled = torch.tensor([[[[0.5, 0.5, 0.0]], [[0.0, 0.2, 0.8]]]])      # [B=1, Hkv=2, 1, N=3]
+    idx = torch.tensor([[[[1, 2]]]], dtype=torch.int32)                  # [1, 1, 1, 2]
+    assert bench.captured_mass(pooled, idx) == pytest.approx((0.5 + 1.0) / 2)
+    pos = [[np.array([0, 1]), np.array([2])]]
+    assert bench.planted_recall(pos, idx.numpy(), 1, 3) == pytest.approx((0.5 + 1.0) / 2)
