@@ -4,8 +4,10 @@
 // Input: non-negative float32 scores (pooled post-softmax probabilities). For
 // non-negative IEEE floats the 32-bit pattern orders like the value and bit 31
 // is clear, so the k-th largest score is found by an MSB-first radix select
-// over bits 30..0: digit histograms in LDS over the exponent (bits 30..23),
-// then bits 22..15, 14..7 and 6..0, each pass narrowing to the bucket that
+// over bits 30..0: digit histograms in LDS over bits 30..20 (the exponent and
+// three mantissa bits, so that probabilities, which cluster in a few
+// octaves, still spread over many bins and the histogram atomics rarely
+// collide), then bits 19..10 and 9..0, each pass narrowing to the bucket that
 // holds the k-th element. That gives the exact threshold
 // pattern and how many keys equal to it are still needed. A final ordered
 // pass then writes, in ascending key order, every key above the threshold and
@@ -21,7 +23,9 @@
 //
 // Decode fuses the pooling: the segment of KV head kv is produced here from
 // the group's scaled logits and row log-sum-exps, sum over heads of
-// exp2(logit - lse2), straight into registers.
+// exp2(logit - lse2), straight into registers. Heads are summed in order; for
+// each head a thread has eight 16-byte loads in flight, which keeps enough
+// bytes moving per compute unit to stream the logits.
 //
 // One set shared by all heads (the non-head-aware ablation) pools first, in a
 // separate pass: decode sums exp2(logit - lse2) over all Hq heads per key;
@@ -34,10 +38,12 @@ namespace kascade {
 
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kWaves = kThreads / 64;
-constexpr int kShift[4] = {23, 15, 7, 0};
-constexpr unsigned kDigitMask[4] = {0xffu, 0xffu, 0xffu, 0x7fu};
+constexpr int kThreads = 1024;  // decode segments and long prefill segments
+constexpr int kSmallThreads = 256;  // prefill segments of at most kRegs * 256 keys
+constexpr int kPasses = 3;  // digits: bits 30..20, 19..10, 9..0
+constexpr int kMaxBins = 2048;
+__device__ __forceinline__ int pass_shift(int pass) { return 20 - 10 * pass; }
+__device__ __forceinline__ int pass_bins(int pass) { return pass == 0 ? 2048 : 1024; }
 
 __device__ __forceinline__ void hist_add(unsigned* hist, unsigned digit, bool active) {
   const uint64_t act = __ballot(active);
@@ -51,8 +57,9 @@ __device__ __forceinline__ void hist_add(unsigned* hist, unsigned digit, bool ac
   if (active && !same) atomicAdd(&hist[digit], 1u);
 }
 
-// Exclusive block-wide prefix count of `flag` over thread order; returns the
-// rank of this thread among flagged threads and the block total.
+// Exclusive block-wide prefix count of `flag` over thread order (NT threads);
+// returns the rank of this thread among flagged threads and the block total.
+template <int NT>
 __device__ __forceinline__ unsigned block_rank(bool flag, unsigned* wave_tot, unsigned& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint64_t mask = __ballot(flag);
@@ -61,7 +68,7 @@ __device__ __forceinline__ unsigned block_rank(bool flag, unsigned* wave_tot, un
   __syncthreads();
   unsigned before = 0, all = 0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
+  for (int w = 0; w < NT / 64; ++w) {
     const unsigned c = wave_tot[w];
     before += w < wave ? c : 0u;
     all += c;
@@ -71,86 +78,8 @@ __device__ __forceinline__ unsigned block_rank(bool flag, unsigned* wave_tot, un
   return before + below;
 }
 
-__device__ void select_segment(const unsigned* keys, int n, int kt, int k, int32_t* out) {
-  __shared__ unsigned hist[256];
-  __shared__ unsigned wave_tot[kWaves];
-  __shared__ unsigned sh_prefix, sh_krem;
-  const int tid = threadIdx.x;
-
-  if (kt >= n) {  // every candidate is kept
-    for (int s = tid; s < k; s += kThreads) out[s] = s < n ? s : -1;
-    return;
-  }
-
-  unsigned prefix = 0, mask = 0, krem = (unsigned)kt;
-#pragma unroll
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = kShift[pass];
-    const unsigned dmask = kDigitMask[pass];
-    for (int i = tid; i < 256; i += kThreads) hist[i] = 0;
-    __syncthreads();
-    for (int j0 = 0; j0 < n; j0 += kThreads) {
-      const int j = j0 + tid;
-      const unsigned u = j < n ? keys[j] : 0u;
-      const bool match = j < n && (u & mask) == prefix;
-      hist_add(hist, (u >> shift) & dmask, match);
-    }
-    __syncthreads();
-    if (tid < 64) {
-      // Lane L covers buckets 255-4L .. 252-4L, i.e. lanes walk from the top.
-      unsigned c[4], local = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        c[i] = hist[255 - 4 * tid - i];
-        local += c[i];
-      }
-      unsigned incl = local;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const unsigned t = __shfl_up(incl, o);
-        if (tid >= o) incl += t;
-      }
-      const unsigned excl = incl - local;
-      if (excl < krem && krem <= incl) {
-        unsigned run = excl;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (run + c[i] >= krem) {
-            sh_prefix = prefix | ((unsigned)(255 - 4 * tid - i) << shift);
-            sh_krem = krem - run;
-            break;
-          }
-          run += c[i];
-        }
-      }
-    }
-    __syncthreads();
-    prefix = sh_prefix;
-    krem = sh_krem;
-    mask |= dmask << shift;
-    __syncthreads();
-  }
-
-  // prefix is the k-th largest pattern; krem keys equal to it are still needed.
-  unsigned base = 0, eq_seen = 0;
-  for (int j0 = 0; j0 < n; j0 += kThreads) {
-    const int j = j0 + tid;
-    const unsigned u = j < n ? keys[j] : 0u;
-    const bool gt = j < n && u > prefix;
-    const bool eq = j < n && u == prefix;
-    unsigned eq_total;
-    const unsigned eq_rank = eq_seen + block_rank(eq, wave_tot, eq_total);
-    const bool sel = gt || (eq && eq_rank < krem);
-    unsigned sel_total;
-    const unsigned pos = base + block_rank(sel, wave_tot, sel_total);
-    if (sel && pos < (unsigned)kt) out[pos] = j;  // bound holds by construction; kept as a guard
-    base += sel_total;
-    eq_seen += eq_total;
-  }
-  for (int s = kt + tid; s < k; s += kThreads) out[s] = -1;
-}
-
-// Exclusive prefix sum of v over thread order (1024 threads); `total` gets the sum.
+// Exclusive prefix sum of v over thread order (NT threads); `total` gets the sum.
+template <int NT>
 __device__ __forceinline__ unsigned block_scan(unsigned v, unsigned* wave_tot, unsigned& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   unsigned incl = v;
@@ -163,7 +92,7 @@ __device__ __forceinline__ unsigned block_scan(unsigned v, unsigned* wave_tot, u
   __syncthreads();
   unsigned before = 0, all = 0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
+  for (int w = 0; w < NT / 64; ++w) {
     const unsigned c = wave_tot[w];
     before += w < wave ? c : 0u;
     all += c;
@@ -173,70 +102,126 @@ __device__ __forceinline__ unsigned block_scan(unsigned v, unsigned* wave_tot, u
   return before + incl - v;
 }
 
+// After a histogram pass over `bins` buckets of the digit at `shift`: find the
+// bucket holding the krem-th largest candidate, counting from the top bucket
+// down, and extend prefix / reduce krem to it. Thread t scans the per = bins/NT
+// buckets bins-1-per*t downwards. Every thread returns the same prefix and krem.
+template <int NT>
+__device__ __forceinline__ void narrow(const unsigned* hist, int bins, int shift, unsigned* wave_tot,
+                                       unsigned* sh, unsigned& prefix, unsigned& krem) {
+  const int tid = threadIdx.x;
+  const int per = bins / NT;
+  const int top = bins - 1 - per * tid;
+  unsigned local = 0;
+  for (int i = 0; i < per; ++i) local += hist[top - i];
+  unsigned total;
+  const unsigned above = block_scan<NT>(local, wave_tot, total);  // candidates in higher buckets
+  if (above < krem && krem <= above + local) {
+    unsigned run = above;
+    for (int i = 0; i < per; ++i) {
+      const unsigned c = hist[top - i];
+      if (krem <= run + c) {
+        sh[0] = prefix | ((unsigned)(top - i) << shift);
+        sh[1] = krem - run;
+        break;
+      }
+      run += c;
+    }
+  }
+  __syncthreads();
+  prefix = sh[0];
+  krem = sh[1];
+}
+
+// Selection over a segment read from memory (any length).
+template <int NT>
+__device__ __forceinline__ void select_segment(const unsigned* keys, int n, int kt, int k, int32_t* out) {
+  __shared__ unsigned hist[kMaxBins];
+  __shared__ unsigned wave_tot[NT / 64];
+  __shared__ unsigned sh[2];
+  const int tid = threadIdx.x;
+
+  if (kt >= n) {  // every candidate is kept
+    for (int s = tid; s < k; s += NT) out[s] = s < n ? s : -1;
+    return;
+  }
+
+  unsigned prefix = 0, mask = 0, krem = (unsigned)kt;
+#pragma unroll
+  for (int pass = 0; pass < kPasses; ++pass) {
+    const int shift = pass_shift(pass), bins = pass_bins(pass);
+    const unsigned dmask = (unsigned)bins - 1u;
+    for (int i = tid; i < bins; i += NT) hist[i] = 0;
+    __syncthreads();
+    for (int j0 = 0; j0 < n; j0 += NT) {
+      const int j = j0 + tid;
+      const unsigned u = j < n ? keys[j] : 0u;
+      const bool match = j < n && (u & mask) == prefix;
+      hist_add(hist, (u >> shift) & dmask, match);
+    }
+    __syncthreads();
+    narrow<NT>(hist, bins, shift, wave_tot, sh, prefix, krem);
+    mask |= dmask << shift;
+  }
+
+  // prefix is the k-th largest pattern; krem keys equal to it are still needed.
+  unsigned base = 0, eq_seen = 0;
+  for (int j0 = 0; j0 < n; j0 += NT) {
+    const int j = j0 + tid;
+    const unsigned u = j < n ? keys[j] : 0u;
+    const bool gt = j < n && u > prefix;
+    const bool eq = j < n && u == prefix;
+    unsigned eq_total;
+    const unsigned eq_rank = eq_seen + block_rank<NT>(eq, wave_tot, eq_total);
+    const bool sel = gt || (eq && eq_rank < krem);
+    unsigned sel_total;
+    const unsigned pos = base + block_rank<NT>(sel, wave_tot, sel_total);
+    if (sel && pos < (unsigned)kt) out[pos] = j;  // bound holds by construction; kept as a guard
+    base += sel_total;
+    eq_seen += eq_total;
+  }
+  for (int s = kt + tid; s < k; s += NT) out[s] = -1;
+}
+
 // Same selection with the segment held in registers, for segments of at most
-// 32768 keys. Thread tid holds keys tid + 1024*i (coalesced loads) for the
-// histogram passes, whose counts do not depend on order. The segment is also
+// kRegs * NT keys. Register i of thread tid holds key key_of<NT>(i, tid): four
+// consecutive keys per group of four registers, so loads can be 16 bytes
+// wide; the histogram passes do not depend on order. The segment is also
 // staged in LDS, one padding word per 32 keys, so that in the final pass
 // thread tid reads its contiguous keys 32*tid .. 32*tid+31 without bank
 // conflicts and two prefix sums over threads order the output.
 constexpr int kRegs = 32;
-constexpr int kStage = kRegs * kThreads + kThreads;  // staged keys plus padding
+template <int NT>
+constexpr int stage_len() { return kRegs * NT + NT; }  // staged keys plus padding
 
 __device__ __forceinline__ int stage_index(int j) { return j + (j >> 5); }
+template <int NT>
+__device__ __forceinline__ int key_of(int i, int tid) { return 4 * (NT * (i >> 2) + tid) + (i & 3); }
 
-__device__ void select_registers(const unsigned (&u)[kRegs], const unsigned* staged, int n, int kt,
-                                 int k, int32_t* out) {
-  __shared__ unsigned hist[256];
-  __shared__ unsigned wave_tot[kWaves];
-  __shared__ unsigned sh_prefix, sh_krem;
+template <int NT>
+__device__ __forceinline__ void select_registers(const unsigned (&u)[kRegs], const unsigned* staged, int n,
+                                                 int kt, int k, int32_t* out) {
+  __shared__ unsigned hist[kMaxBins];
+  __shared__ unsigned wave_tot[NT / 64];
+  __shared__ unsigned sh[2];
   const int tid = threadIdx.x;
   if (kt >= n) {
-    for (int s = tid; s < k; s += kThreads) out[s] = s < n ? s : -1;
+    for (int s = tid; s < k; s += NT) out[s] = s < n ? s : -1;
     return;
   }
   unsigned prefix = 0, mask = 0, krem = (unsigned)kt;
 #pragma unroll
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = kShift[pass];
-    const unsigned dmask = kDigitMask[pass];
-    for (int i = tid; i < 256; i += kThreads) hist[i] = 0;
+  for (int pass = 0; pass < kPasses; ++pass) {
+    const int shift = pass_shift(pass), bins = pass_bins(pass);
+    const unsigned dmask = (unsigned)bins - 1u;
+    for (int i = tid; i < bins; i += NT) hist[i] = 0;
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < kRegs; ++i)
-      hist_add(hist, (u[i] >> shift) & dmask, i * kThreads + tid < n && (u[i] & mask) == prefix);
+      hist_add(hist, (u[i] >> shift) & dmask, key_of<NT>(i, tid) < n && (u[i] & mask) == prefix);
     __syncthreads();
-    if (tid < 64) {
-      unsigned c[4], local = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        c[i] = hist[255 - 4 * tid - i];
-        local += c[i];
-      }
-      unsigned incl = local;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const unsigned t = __shfl_up(incl, o);
-        if (tid >= o) incl += t;
-      }
-      const unsigned excl = incl - local;
-      if (excl < krem && krem <= incl) {
-        unsigned run = excl;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (run + c[i] >= krem) {
-            sh_prefix = prefix | ((unsigned)(255 - 4 * tid - i) << shift);
-            sh_krem = krem - run;
-            break;
-          }
-          run += c[i];
-        }
-      }
-    }
-    __syncthreads();
-    prefix = sh_prefix;
-    krem = sh_krem;
+    narrow<NT>(hist, bins, shift, wave_tot, sh, prefix, krem);
     mask |= dmask << shift;
-    __syncthreads();
   }
   // prefix is the k-th largest pattern; krem keys equal to it are still needed,
   // taken lowest index first.
@@ -250,9 +235,9 @@ __device__ void select_registers(const unsigned (&u)[kRegs], const unsigned* sta
     eq += (j0 + i < n && v[i] == prefix) ? 1u : 0u;
   }
   unsigned total;
-  const unsigned eq_before = block_scan(eq, wave_tot, total);
+  const unsigned eq_before = block_scan<NT>(eq, wave_tot, total);
   const unsigned take = krem > eq_before ? min(krem - eq_before, eq) : 0u;
-  unsigned pos = block_scan(gt + take, wave_tot, total);
+  unsigned pos = block_scan<NT>(gt + take, wave_tot, total);
   unsigned taken = 0;
 #pragma unroll
   for (int i = 0; i < kRegs; ++i) {
@@ -264,67 +249,119 @@ __device__ void select_registers(const unsigned (&u)[kRegs], const unsigned* sta
     }
     if (sel && pos < (unsigned)kt) out[pos++] = j0 + i;  // bound holds by construction
   }
-  for (int s = kt + tid; s < k; s += kThreads) out[s] = -1;
+  for (int s = kt + tid; s < k; s += NT) out[s] = -1;
 }
 
 __global__ __launch_bounds__(kThreads) void topk_decode_kernel(const float* logits, int ld,
                                                                  const float* lse2, int hq,
                                                                  int hkv, int group, int n, int k,
                                                                  float* spill, int32_t* idx) {
+  constexpr int NT = kThreads;
   __shared__ float l2[16];
   const int seg = blockIdx.x, b = seg / hkv, kvh = seg % hkv;
   const int tid = threadIdx.x;
   if (tid < group) l2[tid] = lse2[b * hq + kvh * group + tid];
   __syncthreads();
   const float* lg = logits + (size_t)(b * hq + kvh * group) * ld;
-  auto pooled_at = [&](int j) __attribute__((always_inline)) {
-    float acc = 0.f;
-    for (int g = 0; g < group; ++g) acc += fast_exp2(lg[(size_t)g * ld + j] - l2[g]);
-    return acc;  // the sum over heads ranks keys exactly as the mean does
+  // Pooled scores of keys base + key_of(i, tid) into p[i]: the sum over heads
+  // (it ranks keys exactly as the mean does), heads in order. Rows are ld
+  // floats, a multiple of four, so a 16-byte load that starts below n stays
+  // inside its row; keys at or past n get 0.
+  auto pool_block = [&](int base, float (&p)[kRegs]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kRegs; ++i) p[i] = 0.f;
+    for (int g = 0; g < group; ++g) {
+      const float* row = lg + (size_t)g * ld + base;
+      const float m = l2[g];
+      float4 x[kRegs / 4];
+#pragma unroll
+      for (int q = 0; q < kRegs / 4; ++q) {
+        const int j4 = key_of<NT>(4 * q, tid);
+        x[q] = base + j4 < n ? *reinterpret_cast<const float4*>(row + j4) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int q = 0; q < kRegs / 4; ++q) {
+        p[4 * q + 0] += fast_exp2(x[q].x - m);
+        p[4 * q + 1] += fast_exp2(x[q].y - m);
+        p[4 * q + 2] += fast_exp2(x[q].z - m);
+        p[4 * q + 3] += fast_exp2(x[q].w - m);
+      }
+    }
   };
-  if (n <= kRegs * kThreads) {
-    __shared__ unsigned staged[kStage];
+  if (n <= kRegs * NT) {
+    __shared__ unsigned staged[stage_len<NT>()];
+    float p[kRegs];
+    pool_block(0, p);
     unsigned u[kRegs];
 #pragma unroll
     for (int i = 0; i < kRegs; ++i) {
-      const int j = i * kThreads + tid;
-      u[i] = j < n ? __float_as_uint(pooled_at(j)) : 0u;
+      const int j = key_of<NT>(i, tid);
+      u[i] = j < n ? __float_as_uint(p[i]) : 0u;
       if (j < n) staged[stage_index(j)] = u[i];
     }
     __syncthreads();
-    select_registers(u, staged, n, k, k, idx + (size_t)seg * k);
+    select_registers<NT>(u, staged, n, k, k, idx + (size_t)seg * k);
   } else {
     float* dst = spill + (size_t)seg * n;
-    for (int j = tid; j < n; j += kThreads) dst[j] = pooled_at(j);
+    for (int base = 0; base < n; base += kRegs * NT) {
+      float p[kRegs];
+      pool_block(base, p);
+#pragma unroll
+      for (int i = 0; i < kRegs; ++i) {
+        const int j = base + key_of<NT>(i, tid);
+        if (j < n) dst[j] = p[i];
+      }
+    }
     __threadfence_block();
     __syncthreads();
-    select_segment(reinterpret_cast<const unsigned*>(dst), n, k, k, idx + (size_t)seg * k);
+    select_segment<NT>(reinterpret_cast<const unsigned*>(dst), n, k, k, idx + (size_t)seg * k);
   }
 }
 
-__global__ __launch_bounds__(kThreads) void topk_prefill_kernel(const float* pooled, int hkv,
-                                                                  int n, int tile, int tiles,
-                                                                  size_t ragged, int k,
-                                                                  int32_t* idx) {
-  const int t = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+// Tiles t0 + blockIdx.x of every (b, KV head); NT threads per segment.
+template <int NT>
+__global__ __launch_bounds__(NT) void topk_prefill_kernel(const float* pooled, int hkv, int n, int tile,
+                                                          int tiles, int t0, size_t ragged, int k,
+                                                          int32_t* idx) {
+  const int t = t0 + (int)blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int prefix = min((t + 1) * tile, n);
   const size_t base = (size_t)(b * hkv + kvh) * ragged + (size_t)tile * t * (t + 1) / 2;
   int32_t* out = idx + ((size_t)(b * hkv + kvh) * tiles + t) * k;
   const float* src = pooled + base;
-  if (prefix <= kRegs * kThreads) {
-    __shared__ unsigned staged[kStage];
+  if (prefix <= kRegs * NT) {
+    __shared__ unsigned staged[stage_len<NT>()];
     unsigned u[kRegs];
 #pragma unroll
     for (int i = 0; i < kRegs; ++i) {
-      const int j = i * kThreads + threadIdx.x;
+      const int j = key_of<NT>(i, threadIdx.x);
       u[i] = j < prefix ? __float_as_uint(src[j]) : 0u;
       if (j < prefix) staged[stage_index(j)] = u[i];
     }
     __syncthreads();
-    select_registers(u, staged, prefix, min(k, prefix), k, out);
+    select_registers<NT>(u, staged, prefix, min(k, prefix), k, out);
   } else {
-    select_segment(reinterpret_cast<const unsigned*>(src), prefix, min(k, prefix), k, out);
+    select_segment<NT>(reinterpret_cast<const unsigned*>(src), prefix, min(k, prefix), k, out);
   }
+}
+
+// Segments (b, kv, t) of one ragged pooled layout: tiles whose candidates fit
+// a small workgroup's registers go to 256-thread workgroups (several per
+// compute unit), the longer ones to 1024-thread workgroups.
+hipError_t launch_select_tiles(const float* scores, int batch, int hkv, int n, int tile, size_t ragged,
+                               int k, int32_t* idx, hipStream_t s) {
+  const int tiles = (n + tile - 1) / tile;
+  const int small = min(tiles, (kRegs * kSmallThreads) / tile);  // tiles t < small have prefix <= 8192
+  if (tiles > small) {
+    hipLaunchKernelGGL(topk_prefill_kernel<kThreads>, dim3(tiles - small, hkv, batch), dim3(kThreads), 0, s,
+                       scores, hkv, n, tile, tiles, small, ragged, k, idx);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (small > 0) {
+    hipLaunchKernelGGL(topk_prefill_kernel<kSmallThreads>, dim3(small, hkv, batch), dim3(kSmallThreads), 0,
+                       s, scores, hkv, n, tile, tiles, 0, ragged, k, idx);
+  }
+  return hipGetLastError();
 }
 
 constexpr int kPoolThreads = 256;
@@ -362,9 +399,7 @@ __global__ __launch_bounds__(kPoolThreads) void sum_sets_kernel(const float* poo
 hipError_t launch_topk_rows(const float* scores, int rows, int n, int k, int32_t* idx,
                             hipStream_t s) {
   // A row is a single prefill segment whose tile spans all n keys.
-  hipLaunchKernelGGL(topk_prefill_kernel, dim3(1, 1, rows), dim3(kThreads), 0, s, scores, 1, n, n, 1,
-                     (size_t)n, k, idx);
-  return hipGetLastError();
+  return launch_select_tiles(scores, rows, 1, n, n, (size_t)n, k, idx, s);
 }
 
 hipError_t launch_pool_all_heads(const float* logits, int ld, const float* lse2, int batch, int hq,
@@ -393,10 +428,7 @@ hipError_t launch_topk_decode(const float* logits, int ld, const float* lse2, in
 
 hipError_t launch_topk_prefill(const float* scores, int batch, int hkv, int n, int tile, int k,
                                int32_t* idx, hipStream_t s) {
-  const int tiles = (n + tile - 1) / tile;
-  hipLaunchKernelGGL(topk_prefill_kernel, dim3(tiles, hkv, batch), dim3(kThreads), 0, s, scores,
-                     hkv, n, tile, tiles, prefill_ragged_len(n, tile), k, idx);
-  return hipGetLastError();
+  return launch_select_tiles(scores, batch, hkv, n, tile, prefill_ragged_len(n, tile), k, idx, s);
 }
 
 }  // namespace kascade
