@@ -367,12 +367,13 @@ def accuracy_sweep(w, fractions=SWEEP_K_FRACTIONS, dev="cuda", shared=(False, Tr
 def sweep_workloads():
     """The decode workload at 32K and the 8K prefill workload, the latter with
     its planted keys drifting like the decode one's (70 % kept from layer to
-    layer) so the reuse layers meet new heavy keys; each at the benchmarked
-    planted-row gain (diffuse attention) and at gain 16 (most of the attention
-    on the planted keys)."""
+    layer) so the reuse layers meet new heavy keys, and with 128- and 64-row
+    selection tiles; each at the benchmarked planted-row gain (diffuse
+    attention) and at gain 16 (most of the attention on the planted keys)."""
     dec = synth.WORKLOADS["decode_llama8b_32k"]
     pre = synth.WORKLOADS["prefill_8k"].scaled(share=0.7)
-    return [dec, dec.scaled(gain=16.0), pre, pre.scaled(gain=16.0)]
+    pre64 = pre.scaled(tile=64)
+    return [dec, dec.scaled(gain=16.0), pre, pre.scaled(gain=16.0), pre64, pre64.scaled(gain=16.0)]
 
 
 def main():

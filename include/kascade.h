@@ -92,7 +92,7 @@ typedef struct {
   int32_t q_len;        /* decode: 1; prefill: equal to kv_len */
   int32_t kv_len;       /* N >= 1 */
   int32_t top_k;        /* k >= 1; decode requires k <= N */
-  int32_t q_tile;       /* T (prefill only): 128 */
+  int32_t q_tile;       /* T (prefill only): 64 or 128 */
   float scale;          /* logit scale; <= 0 selects 1/sqrt(d) */
   int32_t dtype;        /* kascade_dtype; prefill requires KASCADE_BF16 */
   int32_t shared_index_set; /* 0: one index set per KV head (head-aware, the
@@ -104,7 +104,7 @@ typedef struct {
 /* Check a problem for an op without touching the GPU. Returns KASCADE_OK,
  * KASCADE_ERR_INVALID or KASCADE_ERR_UNSUPPORTED. Supported: decode with
  * float32 or bfloat16 and d in {64, 128}; prefill with bfloat16, d in
- * {64, 128} and T = 128. */
+ * {64, 128} and T in {64, 128}. */
 int kascade_validate(const kascade_problem* p, int op);
 
 /* Bytes of device workspace the op needs for this problem (0 for an invalid

@@ -58,7 +58,7 @@ int validate(const kascade_problem* p, int op) {
   } else {
     if (p->q_len != p->kv_len) return KASCADE_ERR_INVALID;
     if (p->q_tile < 1) return KASCADE_ERR_INVALID;
-    if (p->q_tile != 128) return KASCADE_ERR_UNSUPPORTED;
+    if (p->q_tile != 64 && p->q_tile != 128) return KASCADE_ERR_UNSUPPORTED;
     if (p->dtype != KASCADE_BF16) return KASCADE_ERR_UNSUPPORTED;
   }
   return KASCADE_OK;

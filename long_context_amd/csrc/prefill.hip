@@ -32,7 +32,7 @@ namespace kascade {
 namespace {
 
 constexpr int kRowsPerWave = 32;   // query rows per wavefront in prefill_attn
-constexpr int kTile = 128;         // query tile: four wavefronts of 32 rows
+constexpr int kTile = 128;         // dense-pass work tile: four wavefronts of 32 rows
 constexpr int kLdsPad = 16;        // bf16 elements of padding per LDS row
 constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (log2 units)
 
@@ -63,8 +63,10 @@ __device__ __forceinline__ lds_bf16x4 lds_read_transposed(const __bf16* p) {
 //   half hf stands for key 16ks + 8(j/4) + 4hf + (j%4); the A operand supplies
 //   V at those keys for d = 32db + l%32, two transposed LDS reads of four
 //   consecutive keys each.
-template <int D, bool GATHER, bool WITH_O, int NH, int KC>
-__global__ __launch_bounds__(256 * NH) void prefill_attn(PrefillArgs a) {
+// TR query rows per workgroup and head (the selection tile in gather mode;
+// kTile in the dense pass), TR / 32 wavefronts per head, NH heads.
+template <int D, bool GATHER, bool WITH_O, int NH, int KC, int TR>
+__global__ __launch_bounds__(64 * (TR / kRowsPerWave) * NH) void prefill_attn(PrefillArgs a) {
   constexpr int kKeyChunk = KC;
   constexpr int kKeyWaves = KC / 64;  // wavefronts that hold the chunk's list entries
   constexpr int C = D / 16;           // 16-element contraction chunks of S^T
@@ -74,7 +76,8 @@ __global__ __launch_bounds__(256 * NH) void prefill_attn(PrefillArgs a) {
   // bytes (two 16-lane groups), so rows are padded by 64 bytes (16 banks):
   // the four rows then cover all 64 banks.
   constexpr int LDV = D + 32;
-  constexpr int THREADS = 256 * NH;
+  constexpr int WPH = TR / kRowsPerWave;                 // wavefronts per head
+  constexpr int THREADS = 64 * WPH * NH;
   constexpr int VPR = D / 8;                             // 16-byte vectors per row
   constexpr int LPT = kKeyChunk * VPR / THREADS;         // vectors per thread per tensor
   static_assert(LPT >= 1 && kKeyChunk * VPR % THREADS == 0, "chunk must split evenly");
@@ -85,23 +88,24 @@ __global__ __launch_bounds__(256 * NH) void prefill_attn(PrefillArgs a) {
   __shared__ int info_s[2][kKeyWaves][4];
 
   // Longest tiles first across all heads and batches: workgroup i takes tile
-  // tiles-1 - i / (B * Hq/NH), so the dispatcher hands out the work in
+  // tiles-1 - i / (B * Hq/NH) of TR rows, so the dispatcher hands out the work in
   // decreasing length and the last workgroups to start are the shortest.
   // Within a tile, u % (B*Hkv) is the (b, KV head) and u / (B*Hkv) the head
   // block of its group: consecutive workgroups, which the dispatcher deals to
   // the 8 XCDs in turn, keep a KV group's head blocks on one XCD and its L2.
   const int units = a.batch * (a.hq / NH);
-  const int t = a.tiles - 1 - (int)blockIdx.x / units;
+  const int wtiles = (a.n + TR - 1) / TR;
+  const int t = wtiles - 1 - (int)blockIdx.x / units;
   const int u = (int)blockIdx.x % units;
   const int kvg = u % (a.batch * a.hkv), member = u / (a.batch * a.hkv);
   const int b = kvg / a.hkv;
   const int hb = (kvg % a.hkv) * (a.group / NH) + member;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-  const int h = hb * NH + wave / 4;
+  const int h = hb * NH + wave / WPH;
   const int kvh = h / a.group;             // the NH heads of a block share one KV head
   const int col = lane & 31, hf = lane >> 5;
-  const int prefix = min((t + 1) * kTile, a.n);
-  const int wrow0 = t * kTile + (wave & 3) * kRowsPerWave;
+  const int prefix = min((t + 1) * TR, a.n);
+  const int wrow0 = t * TR + (wave % WPH) * kRowsPerWave;
   const int wrow_last = min(wrow0 + kRowsPerWave, a.n) - 1;
   const int my_row = wrow0 + col;
   const float sl2 = a.scale_log2;
@@ -337,42 +341,47 @@ __global__ __launch_bounds__(256 * NH) void prefill_attn(PrefillArgs a) {
 constexpr int kPoolWaves = 4;
 constexpr int kPoolKeysPerWave = 64;
 constexpr int kPoolKeys = kPoolWaves * kPoolKeysPerWave;  // keys per workgroup
-constexpr int kPoolBlocks = kTile / 16;                   // 16-row blocks per staged head
 
 // Work items of one (b, KV head) are (tile t, chunk of kPoolKeys candidate keys).
-// Tile t has prefix_t candidates and ceil(prefix_t / 256) = ceil((t+1) / 2)
-// chunks (this also holds for a ragged last tile), so the items before tile t
-// number sum_{u<t} ceil((u+1)/2).
-__host__ __device__ inline int pool_items_before(int t) {
-  const int m = t / 2;
-  return (t & 1) ? (m + 1) * (m + 1) : m * (m + 1);
+// With T-row tiles, tile t is given ceil((t+1) T / 256) chunks (its prefix_t
+// candidates need at most that many; a chunk past a ragged last tile's prefix
+// does nothing), so the items before tile t number
+// sum_{u=1..t} ceil(u / p), p = 256 / T, which is p Q(Q+1)/2 + R(Q+1) for
+// t = Qp + R, 0 <= R < p.
+__host__ __device__ inline int pool_items_before(int t, int tile) {
+  const int p = kPoolKeys / tile;
+  const int q = t / p, r = t % p;
+  return p * q * (q + 1) / 2 + r * (q + 1);
 }
 
-template <int D>
+// TP query rows per tile (the selection tile: 64 or 128).
+template <int D, int TP>
 __global__ __launch_bounds__(64 * kPoolWaves) void prefill_pool(PrefillArgs a, int items, int per_xcd) {
   constexpr int C = D / 32;
   constexpr int LD = D + kLdsPad;
   constexpr int THREADS = 64 * kPoolWaves;
   constexpr int VPR = D / 8;
-  constexpr int LPT = kTile * VPR / THREADS;
-  static_assert(LPT >= 1 && kTile * VPR % THREADS == 0, "tile rows must split evenly");
-  __shared__ __attribute__((aligned(16))) __bf16 qs[2][kTile * LD];
-  __shared__ __attribute__((aligned(16))) float ls[2][kTile];
+  constexpr int LPT = TP * VPR / THREADS;
+  constexpr int kPoolBlocks = TP / 16;  // 16-row blocks per staged head
+  static_assert(LPT >= 1 && TP * VPR % THREADS == 0, "tile rows must split evenly");
+  __shared__ __attribute__((aligned(16))) __bf16 qs[2][TP * LD];
+  __shared__ __attribute__((aligned(16))) float ls[2][TP];
 
   // Workgroups go round-robin to the 8 XCDs; items are dealt so that each XCD
   // takes a contiguous run (the chunks of a tile share its query rows in L2).
   const int item = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
   if (item >= items) return;
-  int t = max(0, (int)(2.0f * sqrtf((float)item)) - 1);
-  while (pool_items_before(t + 1) <= item) ++t;
-  while (t > 0 && pool_items_before(t) > item) --t;
-  const int kbase = (item - pool_items_before(t)) * kPoolKeys;
+  // items_before(t) ~ t^2 T / 512: start from that estimate, then step.
+  int t = max(0, (int)sqrtf(512.0f / TP * (float)item) - 1);
+  while (pool_items_before(t + 1, TP) <= item) ++t;
+  while (t > 0 && pool_items_before(t, TP) > item) --t;
+  const int kbase = (item - pool_items_before(t, TP)) * kPoolKeys;
   const int kvh = blockIdx.z % a.hkv, b = blockIdx.z / a.hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int n16 = lane & 15, qg = lane >> 4;
   const int wkey0 = kbase + wave * kPoolKeysPerWave;
-  const int row0 = t * kTile;
-  const int prefix = min(row0 + kTile, a.n);
+  const int row0 = t * TP;
+  const int prefix = min(row0 + TP, a.n);
   const float sl2 = a.scale_log2;
 
   // K^T operands of this wave's 64 keys (keys past N read row 0 and are never
@@ -400,7 +409,7 @@ __global__ __launch_bounds__(64 * kPoolWaves) void prefill_pool(PrefillArgs a, i
       const int row = slot / VPR, col = (slot % VPR) * 8;
       qr[i] = load_bf16x8(qh + (size_t)min(row0 + row, a.n - 1) * D + col);
     }
-    if (tid < kTile) {
+    if (tid < TP) {
       const int row = row0 + tid;
       // Rows past N get +inf so that every probability they add is 0.
       lr = row < a.n ? a.lse2[(size_t)(b * a.hq + h) * a.n + row] : INFINITY;
@@ -413,7 +422,7 @@ __global__ __launch_bounds__(64 * kPoolWaves) void prefill_pool(PrefillArgs a, i
       const int row = slot / VPR, col = (slot % VPR) * 8;
       *reinterpret_cast<bf16x8*>(&qs[buf][row * LD + col]) = qr[i];
     }
-    if (tid < kTile) ls[buf][tid] = lr;
+    if (tid < TP) ls[buf][tid] = lr;
   };
   auto read_q = [&](int buf, int rb, bf16x8 (&aq)[C], f32x4& lse) __attribute__((always_inline)) {
 #pragma unroll
@@ -494,8 +503,8 @@ __global__ __launch_bounds__(64 * kPoolWaves) void prefill_pool(PrefillArgs a, i
     if (step + 2 < a.group) fetch(step + 2);
   }
 
-  const size_t ragged = prefill_ragged_len(a.n, kTile);
-  float* dst = a.pooled + (size_t)(b * a.hkv + kvh) * ragged + (size_t)kTile * t * (t + 1) / 2;
+  const size_t ragged = prefill_ragged_len(a.n, TP);
+  float* dst = a.pooled + (size_t)(b * a.hkv + kvh) * ragged + (size_t)TP * t * (t + 1) / 2;
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) {
     const float v = group4_sum(colsum[kt]);
@@ -511,41 +520,60 @@ __global__ void lse2_to_lse_kernel(const float* lse2, float* lse, size_t count) 
 
 }  // namespace
 
-template <int D, bool GATHER, bool WITH_O>
+template <int D, bool GATHER, bool WITH_O, int TR>
 hipError_t launch_attn(const PrefillArgs& a, hipStream_t s) {
-  // Reuse layers: two heads of a GQA group per workgroup share every gathered
-  // K/V chunk, staged 128 keys at a time so each gather has a long step of
-  // work to land behind. Dense pass: one head per workgroup and 64-key steps,
-  // two workgroups per compute unit.
-  if (GATHER && a.group % 2 == 0) {
-    dim3 grid(a.tiles * a.batch * (a.hq / 2));
-    hipLaunchKernelGGL((prefill_attn<D, GATHER, WITH_O, 2, 128>), grid, dim3(512), 0, s, a);
+  // Reuse layers: the heads of a GQA group that fill eight wavefronts (two
+  // heads of 128 rows, or four of 64) share every gathered K/V chunk, staged
+  // 128 keys at a time so each gather has a long step of work to land behind.
+  // Dense pass: one head per workgroup and 64-key steps, two workgroups per
+  // compute unit.
+  constexpr int WPH = TR / kRowsPerWave;
+  constexpr int NHG = 8 / WPH;
+  const int wtiles = (a.n + TR - 1) / TR;
+  if (GATHER && a.group % NHG == 0) {
+    dim3 grid(wtiles * a.batch * (a.hq / NHG));
+    hipLaunchKernelGGL((prefill_attn<D, GATHER, WITH_O, NHG, 128, TR>), grid, dim3(64 * WPH * NHG), 0, s, a);
+  } else if (GATHER && NHG > 2 && a.group % 2 == 0) {
+    dim3 grid(wtiles * a.batch * (a.hq / 2));
+    hipLaunchKernelGGL((prefill_attn<D, GATHER, WITH_O, 2, 64, TR>), grid, dim3(64 * WPH * 2), 0, s, a);
   } else {
-    dim3 grid(a.tiles * a.batch * a.hq);
-    hipLaunchKernelGGL((prefill_attn<D, GATHER, WITH_O, 1, 64>), grid, dim3(256), 0, s, a);
+    dim3 grid(wtiles * a.batch * a.hq);
+    hipLaunchKernelGGL((prefill_attn<D, GATHER, WITH_O, 1, 64, TR>), grid, dim3(64 * WPH), 0, s, a);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_prefill_dense(const PrefillArgs& a, hipStream_t s) {
   const bool with_o = a.out != nullptr;
-  if (a.d == 128) return with_o ? launch_attn<128, false, true>(a, s) : launch_attn<128, false, false>(a, s);
-  if (a.d == 64) return with_o ? launch_attn<64, false, true>(a, s) : launch_attn<64, false, false>(a, s);
+  // The row log-sum-exp and the dense output do not depend on the selection
+  // tile, so the dense pass always works in kTile-row tiles.
+  if (a.d == 128)
+    return with_o ? launch_attn<128, false, true, kTile>(a, s) : launch_attn<128, false, false, kTile>(a, s);
+  if (a.d == 64)
+    return with_o ? launch_attn<64, false, true, kTile>(a, s) : launch_attn<64, false, false, kTile>(a, s);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_prefill_reuse(const PrefillArgs& a, hipStream_t s) {
-  if (a.d == 128) return launch_attn<128, true, true>(a, s);
-  if (a.d == 64) return launch_attn<64, true, true>(a, s);
+  if (a.tile == 128) {
+    if (a.d == 128) return launch_attn<128, true, true, 128>(a, s);
+    if (a.d == 64) return launch_attn<64, true, true, 128>(a, s);
+  } else if (a.tile == 64) {
+    if (a.d == 128) return launch_attn<128, true, true, 64>(a, s);
+    if (a.d == 64) return launch_attn<64, true, true, 64>(a, s);
+  }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_prefill_pool(const PrefillArgs& a, hipStream_t s) {
-  const int items = pool_items_before(a.tiles);
+  const int items = pool_items_before(a.tiles, a.tile);
   const int per_xcd = (items + 7) / 8;
   dim3 grid(8 * per_xcd, 1, a.hkv * a.batch);
-  if (a.d == 128) hipLaunchKernelGGL(prefill_pool<128>, grid, dim3(64 * kPoolWaves), 0, s, a, items, per_xcd);
-  else if (a.d == 64) hipLaunchKernelGGL(prefill_pool<64>, grid, dim3(64 * kPoolWaves), 0, s, a, items, per_xcd);
+  dim3 block(64 * kPoolWaves);
+  if (a.tile == 128 && a.d == 128) hipLaunchKernelGGL((prefill_pool<128, 128>), grid, block, 0, s, a, items, per_xcd);
+  else if (a.tile == 128 && a.d == 64) hipLaunchKernelGGL((prefill_pool<64, 128>), grid, block, 0, s, a, items, per_xcd);
+  else if (a.tile == 64 && a.d == 128) hipLaunchKernelGGL((prefill_pool<128, 64>), grid, block, 0, s, a, items, per_xcd);
+  else if (a.tile == 64 && a.d == 64) hipLaunchKernelGGL((prefill_pool<64, 64>), grid, block, 0, s, a, items, per_xcd);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

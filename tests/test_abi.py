@@ -53,8 +53,9 @@ def test_validate_accepts_supported_problems(L):
             assert L.validate(_prob(dtype=dt, head_dim=d), K.OP_ANCHOR_DECODE) == K.OK
             assert L.validate(_prob(dtype=dt, head_dim=d), K.OP_REUSE_DECODE) == K.OK
     for d in (64, 128):
-        assert L.validate(_prefill(head_dim=d), K.OP_ANCHOR_PREFILL) == K.OK
-        assert L.validate(_prefill(head_dim=d), K.OP_REUSE_PREFILL) == K.OK
+        for tile in (64, 128):
+            assert L.validate(_prefill(head_dim=d, q_tile=tile), K.OP_ANCHOR_PREFILL) == K.OK
+            assert L.validate(_prefill(head_dim=d, q_tile=tile), K.OP_REUSE_PREFILL) == K.OK
     assert L.validate(_prob(top_k=4096), K.OP_ANCHOR_DECODE) == K.OK          # k = N
     assert L.validate(_prefill(top_k=5000), K.OP_ANCHOR_PREFILL) == K.OK      # k > N is fine in prefill
     assert L.validate(_prob(num_q_heads=32, num_kv_heads=2), K.OP_REUSE_DECODE) == K.OK  # G = 16
@@ -72,7 +73,8 @@ def test_validate_accepts_supported_problems(L):
     (dict(scale=float("nan")), K.OP_REUSE_DECODE, K.ERR_INVALID),
     (dict(q_len=1000, kv_len=999), K.OP_ANCHOR_PREFILL, K.ERR_INVALID),
     (dict(q_len=1000, kv_len=1000, dtype=K.F32), K.OP_ANCHOR_PREFILL, K.ERR_UNSUPPORTED),
-    (dict(q_len=1000, kv_len=1000, q_tile=64), K.OP_REUSE_PREFILL, K.ERR_UNSUPPORTED),
+    (dict(q_len=1000, kv_len=1000, q_tile=32), K.OP_REUSE_PREFILL, K.ERR_UNSUPPORTED),
+    (dict(q_len=1000, kv_len=1000, q_tile=96), K.OP_ANCHOR_PREFILL, K.ERR_UNSUPPORTED),
     (dict(q_len=1000, kv_len=1000, q_tile=0), K.OP_REUSE_PREFILL, K.ERR_INVALID),
 ])
 def test_validate_rejects(L, kw, op, status):
@@ -98,6 +100,11 @@ def test_workspace_sizes(L):
     tiles = -(-1000 // 128)
     ragged = 128 * (tiles - 1) * tiles // 2 + 1000
     assert ap >= 4 * (2 * 8 * 1000 + 2 * 2 * ragged)
+    # 64-row tiles: twice the tiles, and a longer ragged layout
+    ap64 = L.workspace_bytes(_prefill(q_tile=64), K.OP_ANCHOR_PREFILL)
+    tiles = -(-1000 // 64)
+    ragged64 = 64 * (tiles - 1) * tiles // 2 + 1000
+    assert ap64 >= 4 * (2 * 8 * 1000 + 2 * 2 * ragged64) and ap64 > ap
 
 
 def test_status_strings(L):

@@ -34,6 +34,13 @@ CASES = {
     "k_below_tile": _small("k_below_tile", wid=954, n=450, k=40),
     "single_short_tile": _small("single_short_tile", wid=955, n=77, k=32, planted=2),
     "n1": _small("n1", wid=956, n=1, k=1, planted=0, sinks=0),
+    # 64-row selection tiles: four heads per reuse workgroup (G = 4, 8), two
+    # heads (G = 2), one head (G = 1)
+    "t64_d128_ragged": _small("t64_d128_ragged", wid=957, tile=64),
+    "t64_d64_g8": _small("t64_d64_g8", wid=958, hq=16, hkv=2, d=64, n=700, k=160, tile=64),
+    "t64_g2": _small("t64_g2", wid=959, hq=4, hkv=2, n=520, k=100, tile=64),
+    "t64_g1_batch2": _small("t64_g1_batch2", wid=962, batch=2, hq=2, hkv=2, n=300, k=50, tile=64),
+    "t64_k_below_tile": _small("t64_k_below_tile", wid=963, n=450, k=40, tile=64),
 }
 
 
@@ -161,6 +168,12 @@ def test_prefill_8k_sampled(lib, orc):
     w = synth.WORKLOADS["prefill_8k"]
     log("[prefill] case=prefill_8k full size, sampled tiles and rows")
     _sampled_full(orc, w, [(0, 0), (0, 7), (3, 8), (5, 31), (7, 63)], 2048, seed=31)
+
+
+def test_prefill_8k_t64_sampled(lib, orc):
+    w = synth.WORKLOADS["prefill_8k"].scaled(tile=64)
+    log("[prefill] case=prefill_8k with 64-row tiles, sampled tiles and rows")
+    _sampled_full(orc, w, [(0, 0), (1, 15), (3, 16), (5, 63), (7, 127)], 2048, seed=33)
 
 
 def test_prefill_32k_sampled(lib, orc):

@@ -45,6 +45,7 @@ PREFILL = {
     "d128_ragged": _prefill("d128_ragged"),
     "d64_batch2_hkv4": _prefill("d64_batch2_hkv4", wid=996, batch=2, hkv=4, d=64, n=700, k=100),
     "k_below_tile": _prefill("k_below_tile", wid=997, n=450, k=40),
+    "t64_ragged": _prefill("t64_ragged", wid=989, n=700, k=100, tile=64),
 }
 
 

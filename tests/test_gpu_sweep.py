@@ -20,6 +20,9 @@ CASES = {
                              n=4096, k=256, tile=1, dtype="bf16", layers=3, planted=32, share=0.7),
     "prefill": synth.Workload(name="sweep_prefill", wid=982, phase="prefill", batch=1, hq=8, hkv=2, d=128,
                               n=1088, k=256, tile=128, dtype="bf16", layers=3, planted=32, share=0.7, sinks=4),
+    "prefill_t64": synth.Workload(name="sweep_prefill_t64", wid=983, phase="prefill", batch=1, hq=8, hkv=2,
+                                  d=128, n=1000, k=256, tile=64, dtype="bf16", layers=3, planted=32, share=0.7,
+                                  sinks=4),
 }
 
 
