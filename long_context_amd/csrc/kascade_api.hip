@@ -84,7 +84,7 @@ DecodeSplit decode_split(const kascade_problem* p, int len, bool dense) {
 
 struct DecodeWorkspace {
   DecodeSplit split;
-  size_t part_ml, part_o, logits, lse2, pooled, total;  // byte offsets
+  size_t part_ml, part_o, logits, lse2, pooled, cand_val, cand_idx, total;  // byte offsets
 };
 
 DecodeWorkspace decode_workspace(const kascade_problem* p, int op) {
@@ -102,8 +102,16 @@ DecodeWorkspace decode_workspace(const kascade_problem* p, int op) {
     off += align_up(rows * decode_logits_ld(p->kv_len) * sizeof(float));
     w.lse2 = off;
     off += align_up(rows * sizeof(float));
-    w.pooled = off;
-    off += align_up((size_t)p->batch * p->num_kv_heads * p->kv_len * sizeof(float));
+    if (p->shared_index_set) {  // one pooled row per batch row
+      w.pooled = off;
+      off += align_up((size_t)p->batch * p->kv_len * sizeof(float));
+    } else {  // sub-segment candidates of long segments
+      const size_t cand = (size_t)p->batch * p->num_kv_heads * topk_decode_candidates(p->kv_len, p->top_k);
+      w.cand_val = off;
+      off += align_up(cand * sizeof(float));
+      w.cand_idx = off;
+      off += align_up(cand * sizeof(int32_t));
+    }
   }
   w.total = off;
   return w;
@@ -301,7 +309,9 @@ int kascade_anchor_decode(const kascade_problem* p, const void* q, const void* k
     KASCADE_TRY("topk_rows", launch_topk_rows(pooled, p->batch, a.n, p->top_k, idx, s));
   } else {
     KASCADE_TRY("topk_decode", launch_topk_decode(a.logits, a.logits_ld, lse2, p->batch, a.hq, a.hkv,
-                                                  a.group, a.n, p->top_k, pooled, idx, s));
+                                                  a.group, a.n, p->top_k,
+                                                  reinterpret_cast<float*>(ws + w.cand_val),
+                                                  reinterpret_cast<int32_t*>(ws + w.cand_idx), idx, s));
   }
   return KASCADE_OK;
 }

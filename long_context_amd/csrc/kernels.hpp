@@ -43,10 +43,14 @@ hipError_t launch_decode_combine(const float* part_ml, const float* part_o, int 
 // Exact top-k of non-negative float scores per segment, ascending indices,
 // lower index first among equal scores, -1 padding up to k.
 // Decode: segment (b, kv) is pooled here from the group's logits [., ld] and
-// lse2; above 32768 keys the scores go through `spill` [B*Hkv*n].
+// lse2, in sub-segments of 32768 keys; above one sub-segment the per-sub
+// selections go through candidate arrays of topk_decode_candidates(n, k)
+// entries per segment (cand_val float, cand_idx int32), then a merge.
+int topk_decode_subsegments(int n);
+size_t topk_decode_candidates(int n, int k);
 hipError_t launch_topk_decode(const float* logits, int ld, const float* lse2, int batch, int hq,
-                              int hkv, int group, int n, int k, float* spill, int32_t* idx,
-                              hipStream_t s);
+                              int hkv, int group, int n, int k, float* cand_val, int32_t* cand_idx,
+                              int32_t* idx, hipStream_t s);
 // Rows of n scores each, one selection per row: [rows, n] -> idx [rows, k].
 hipError_t launch_topk_rows(const float* scores, int rows, int n, int k, int32_t* idx,
                             hipStream_t s);

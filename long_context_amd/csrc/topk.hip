@@ -133,16 +133,38 @@ __device__ __forceinline__ void narrow(const unsigned* hist, int bins, int shift
   krem = sh[1];
 }
 
+// Where a selected position j of a segment goes: the key written to the output
+// is remap[j] when a remap table is given, else key_base + j; vals (optional)
+// receives the selected scores in the same order.
+template <bool REMAP, bool VALS>
+struct SelectOut {
+  int32_t* idx;
+  int key_base;
+  const int32_t* remap;
+  float* vals;
+  __device__ __forceinline__ void put(unsigned pos, int j, unsigned bits) const {
+    idx[pos] = REMAP ? remap[j] : key_base + j;
+    if (VALS) vals[pos] = __uint_as_float(bits);
+  }
+};
+using PlainOut = SelectOut<false, false>;   // positions are the keys
+using CandOut = SelectOut<false, true>;     // keys offset by key_base, scores kept
+using RemapOut = SelectOut<true, false>;    // keys looked up from a table
+
 // Selection over a segment read from memory (any length).
-template <int NT>
-__device__ __forceinline__ void select_segment(const unsigned* keys, int n, int kt, int k, int32_t* out) {
+template <int NT, class Out>
+__device__ __forceinline__ void select_segment(const unsigned* keys, int n, int kt, int k, Out so) {
+  int32_t* out = so.idx;
   __shared__ unsigned hist[kMaxBins];
   __shared__ unsigned wave_tot[NT / 64];
   __shared__ unsigned sh[2];
   const int tid = threadIdx.x;
 
   if (kt >= n) {  // every candidate is kept
-    for (int s = tid; s < k; s += NT) out[s] = s < n ? s : -1;
+    for (int s = tid; s < k; s += NT) {
+      if (s < n) so.put(s, s, keys[s]);
+      else out[s] = -1;
+    }
     return;
   }
 
@@ -176,7 +198,7 @@ __device__ __forceinline__ void select_segment(const unsigned* keys, int n, int 
     const bool sel = gt || (eq && eq_rank < krem);
     unsigned sel_total;
     const unsigned pos = base + block_rank<NT>(sel, wave_tot, sel_total);
-    if (sel && pos < (unsigned)kt) out[pos] = j;  // bound holds by construction; kept as a guard
+    if (sel && pos < (unsigned)kt) so.put(pos, j, u);  // bound holds by construction; kept as a guard
     base += sel_total;
     eq_seen += eq_total;
   }
@@ -198,15 +220,19 @@ __device__ __forceinline__ int stage_index(int j) { return j + (j >> 5); }
 template <int NT>
 __device__ __forceinline__ int key_of(int i, int tid) { return 4 * (NT * (i >> 2) + tid) + (i & 3); }
 
-template <int NT>
+template <int NT, class Out>
 __device__ __forceinline__ void select_registers(const unsigned (&u)[kRegs], const unsigned* staged, int n,
-                                                 int kt, int k, int32_t* out) {
+                                                 int kt, int k, Out so) {
+  int32_t* out = so.idx;
   __shared__ unsigned hist[kMaxBins];
   __shared__ unsigned wave_tot[NT / 64];
   __shared__ unsigned sh[2];
   const int tid = threadIdx.x;
   if (kt >= n) {
-    for (int s = tid; s < k; s += NT) out[s] = s < n ? s : -1;
+    for (int s = tid; s < k; s += NT) {
+      if (s < n) so.put(s, s, staged[stage_index(s)]);
+      else out[s] = -1;
+    }
     return;
   }
   unsigned prefix = 0, mask = 0, krem = (unsigned)kt;
@@ -247,19 +273,36 @@ __device__ __forceinline__ void select_registers(const unsigned (&u)[kRegs], con
       sel = true;
       ++taken;
     }
-    if (sel && pos < (unsigned)kt) out[pos++] = j0 + i;  // bound holds by construction
+    if (sel && pos < (unsigned)kt) so.put(pos++, j0 + i, v[i]);  // bound holds by construction
   }
   for (int s = kt + tid; s < k; s += NT) out[s] = -1;
 }
 
-__global__ __launch_bounds__(kThreads) void topk_decode_kernel(const float* logits, int ld,
+// Decode selection in sub-segments of kSub = kRegs * 1024 keys, one workgroup
+// each:
+// workgroup (seg, sub) pools keys [sub * kSub, ...) of segment seg = (b, KV
+// head) into registers and selects their exact top-k. With one sub-segment
+// that is the answer; otherwise the selected keys and scores go to the
+// candidate arrays (sub-segment sub at offset sub * min(k, kSub), in key
+// order) and topk_merge_kernel selects among them. Every key of the
+// segment's top-k is among its own sub-segment's top-k (fewer than k keys
+// precede it there), so the merge is exact.
+constexpr int kDecodeThreads = kThreads;
+constexpr int kSub = kRegs * kDecodeThreads;
+
+template <bool WHOLE>
+__global__ __launch_bounds__(kDecodeThreads) void topk_decode_kernel(const float* logits, int ld,
                                                                  const float* lse2, int hq,
                                                                  int hkv, int group, int n, int k,
-                                                                 float* spill, int32_t* idx) {
-  constexpr int NT = kThreads;
+                                                                 int nsub, float* cand_val,
+                                                                 int32_t* cand_idx, int32_t* idx) {
+  constexpr int NT = kDecodeThreads;
   __shared__ float l2[16];
-  const int seg = blockIdx.x, b = seg / hkv, kvh = seg % hkv;
+  const int seg = (int)blockIdx.x / nsub, sub = (int)blockIdx.x % nsub;
+  const int b = seg / hkv, kvh = seg % hkv;
   const int tid = threadIdx.x;
+  const int base = sub * kSub;
+  const int n_sub = min(kSub, n - base);
   if (tid < group) l2[tid] = lse2[b * hq + kvh * group + tid];
   __syncthreads();
   const float* lg = logits + (size_t)(b * hq + kvh * group) * ld;
@@ -267,54 +310,76 @@ __global__ __launch_bounds__(kThreads) void topk_decode_kernel(const float* logi
   // (it ranks keys exactly as the mean does), heads in order. Rows are ld
   // floats, a multiple of four, so a 16-byte load that starts below n stays
   // inside its row; keys at or past n get 0.
-  auto pool_block = [&](int base, float (&p)[kRegs]) __attribute__((always_inline)) {
+  __shared__ unsigned staged[stage_len<NT>()];
+  float p[kRegs];
 #pragma unroll
-    for (int i = 0; i < kRegs; ++i) p[i] = 0.f;
-    for (int g = 0; g < group; ++g) {
-      const float* row = lg + (size_t)g * ld + base;
-      const float m = l2[g];
-      float4 x[kRegs / 4];
+  for (int i = 0; i < kRegs; ++i) p[i] = 0.f;
+  for (int g = 0; g < group; ++g) {
+    const float* row = lg + (size_t)g * ld + base;
+    const float m = l2[g];
+    float4 x[kRegs / 4];
 #pragma unroll
-      for (int q = 0; q < kRegs / 4; ++q) {
-        const int j4 = key_of<NT>(4 * q, tid);
-        x[q] = base + j4 < n ? *reinterpret_cast<const float4*>(row + j4) : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-#pragma unroll
-      for (int q = 0; q < kRegs / 4; ++q) {
-        p[4 * q + 0] += fast_exp2(x[q].x - m);
-        p[4 * q + 1] += fast_exp2(x[q].y - m);
-        p[4 * q + 2] += fast_exp2(x[q].z - m);
-        p[4 * q + 3] += fast_exp2(x[q].w - m);
-      }
+    for (int q = 0; q < kRegs / 4; ++q) {
+      const int j4 = key_of<NT>(4 * q, tid);
+      x[q] = j4 < n_sub ? *reinterpret_cast<const float4*>(row + j4) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-  };
-  if (n <= kRegs * NT) {
+#pragma unroll
+    for (int q = 0; q < kRegs / 4; ++q) {
+      p[4 * q + 0] += fast_exp2(x[q].x - m);
+      p[4 * q + 1] += fast_exp2(x[q].y - m);
+      p[4 * q + 2] += fast_exp2(x[q].z - m);
+      p[4 * q + 3] += fast_exp2(x[q].w - m);
+    }
+  }
+  unsigned u[kRegs];
+#pragma unroll
+  for (int i = 0; i < kRegs; ++i) {
+    const int j = key_of<NT>(i, tid);
+    u[i] = j < n_sub ? __float_as_uint(p[i]) : 0u;
+    if (j < n_sub) staged[stage_index(j)] = u[i];
+  }
+  __syncthreads();
+  // One sub-segment (WHOLE): the final sets. Several: this sub-segment's candidates.
+  if constexpr (WHOLE) {
+    select_registers<NT>(u, staged, n_sub, k, k, PlainOut{idx + (size_t)seg * k, 0, nullptr, nullptr});
+  } else {
+    const size_t off = ((size_t)seg * nsub + sub) * min(k, kSub);
+    const int kc = min(k, n_sub);
+    select_registers<NT>(u, staged, n_sub, kc, kc, CandOut{cand_idx + off, base, nullptr, cand_val + off});
+  }
+}
+
+// Final selection of segment seg among its candidates (see topk_decode_kernel):
+// m = (nsub - 1) * min(k, kSub) + min(k, keys of the last sub-segment)
+// candidates, stored in key order; NT threads (256 while m fits their
+// registers, else 1024).
+__host__ __device__ inline int merge_candidates(int n, int k, int nsub) {
+  const int kmax = k < kSub ? k : kSub, last = n - (nsub - 1) * kSub;
+  return (nsub - 1) * kmax + (k < last ? k : last);
+}
+
+template <int NT>
+__global__ __launch_bounds__(NT) void topk_merge_kernel(const float* cand_val, const int32_t* cand_idx,
+                                                        int n, int k, int nsub, int32_t* idx) {
+  const int seg = blockIdx.x;
+  const int kmax = min(k, kSub);
+  const int m = merge_candidates(n, k, nsub);
+  const float* vals = cand_val + (size_t)seg * nsub * kmax;
+  const int32_t* keys = cand_idx + (size_t)seg * nsub * kmax;
+  int32_t* out = idx + (size_t)seg * k;
+  if (m <= kRegs * NT) {
     __shared__ unsigned staged[stage_len<NT>()];
-    float p[kRegs];
-    pool_block(0, p);
     unsigned u[kRegs];
 #pragma unroll
     for (int i = 0; i < kRegs; ++i) {
-      const int j = key_of<NT>(i, tid);
-      u[i] = j < n ? __float_as_uint(p[i]) : 0u;
-      if (j < n) staged[stage_index(j)] = u[i];
+      const int j = key_of<NT>(i, threadIdx.x);
+      u[i] = j < m ? __float_as_uint(vals[j]) : 0u;
+      if (j < m) staged[stage_index(j)] = u[i];
     }
     __syncthreads();
-    select_registers<NT>(u, staged, n, k, k, idx + (size_t)seg * k);
+    select_registers<NT>(u, staged, m, k, k, RemapOut{out, 0, keys, nullptr});
   } else {
-    float* dst = spill + (size_t)seg * n;
-    for (int base = 0; base < n; base += kRegs * NT) {
-      float p[kRegs];
-      pool_block(base, p);
-#pragma unroll
-      for (int i = 0; i < kRegs; ++i) {
-        const int j = base + key_of<NT>(i, tid);
-        if (j < n) dst[j] = p[i];
-      }
-    }
-    __threadfence_block();
-    __syncthreads();
-    select_segment<NT>(reinterpret_cast<const unsigned*>(dst), n, k, k, idx + (size_t)seg * k);
+    select_segment<NT>(reinterpret_cast<const unsigned*>(vals), m, k, k, RemapOut{out, 0, keys, nullptr});
   }
 }
 
@@ -338,9 +403,10 @@ __global__ __launch_bounds__(NT) void topk_prefill_kernel(const float* pooled, i
       if (j < prefix) staged[stage_index(j)] = u[i];
     }
     __syncthreads();
-    select_registers<NT>(u, staged, prefix, min(k, prefix), k, out);
+    select_registers<NT>(u, staged, prefix, min(k, prefix), k, PlainOut{out, 0, nullptr, nullptr});
   } else {
-    select_segment<NT>(reinterpret_cast<const unsigned*>(src), prefix, min(k, prefix), k, out);
+    select_segment<NT>(reinterpret_cast<const unsigned*>(src), prefix, min(k, prefix), k,
+                       PlainOut{out, 0, nullptr, nullptr});
   }
 }
 
@@ -418,11 +484,31 @@ hipError_t launch_sum_sets(const float* pooled, int batch, int hkv, size_t len, 
   return hipGetLastError();
 }
 
+int topk_decode_subsegments(int n) { return (n + kSub - 1) / kSub; }
+
+size_t topk_decode_candidates(int n, int k) {
+  const int nsub = topk_decode_subsegments(n);
+  return nsub > 1 ? (size_t)nsub * (size_t)min(k, kSub) : 0;
+}
+
 hipError_t launch_topk_decode(const float* logits, int ld, const float* lse2, int batch, int hq,
-                              int hkv, int group, int n, int k, float* spill, int32_t* idx,
-                              hipStream_t s) {
-  hipLaunchKernelGGL(topk_decode_kernel, dim3(batch * hkv), dim3(kThreads), 0, s, logits, ld, lse2,
-                     hq, hkv, group, n, k, spill, idx);
+                              int hkv, int group, int n, int k, float* cand_val, int32_t* cand_idx,
+                              int32_t* idx, hipStream_t s) {
+  const int nsub = topk_decode_subsegments(n);
+  if (nsub == 1)
+    hipLaunchKernelGGL(topk_decode_kernel<true>, dim3(batch * hkv), dim3(kDecodeThreads), 0, s, logits, ld,
+                       lse2, hq, hkv, group, n, k, nsub, cand_val, cand_idx, idx);
+  else
+    hipLaunchKernelGGL(topk_decode_kernel<false>, dim3(batch * hkv * nsub), dim3(kDecodeThreads), 0, s, logits,
+                       ld, lse2, hq, hkv, group, n, k, nsub, cand_val, cand_idx, idx);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nsub == 1) return e;
+  if (merge_candidates(n, k, nsub) <= kRegs * kSmallThreads)
+    hipLaunchKernelGGL(topk_merge_kernel<kSmallThreads>, dim3(batch * hkv), dim3(kSmallThreads), 0, s, cand_val,
+                       cand_idx, n, k, nsub, idx);
+  else
+    hipLaunchKernelGGL(topk_merge_kernel<kThreads>, dim3(batch * hkv), dim3(kThreads), 0, s, cand_val, cand_idx,
+                       n, k, nsub, idx);
   return hipGetLastError();
 }
 

@@ -94,8 +94,14 @@ def test_workspace_sizes(L):
     rp = L.workspace_bytes(_prefill(), K.OP_REUSE_PREFILL)
     assert ad > 0 and rd > 0 and ap > 0 and rp == 0
     assert ad % 256 == 0 and rd % 256 == 0 and ap % 256 == 0
-    # anchor decode holds at least the fp32 logits and pooled scores
-    assert ad >= 4 * (2 * 8 * 4096 + 2 * 2 * 4096)
+    # anchor decode holds at least the fp32 logits
+    assert ad >= 4 * (2 * 8 * 4096)
+    # past one 32768-key sub-segment it also holds the selection candidates:
+    # per (b, KV head) and sub-segment, min(k, 32768) (score, key) pairs
+    ws_k = {kk: L.workspace_bytes(_prob(kv_len=131072, top_k=kk), K.OP_ANCHOR_DECODE) for kk in (1024, 2048)}
+    assert ws_k[2048] - ws_k[1024] == 2 * 2 * 4 * 1024 * 8          # B * Hkv * 4 sub-segments * 1024 * 8 B
+    short = {kk: L.workspace_bytes(_prob(kv_len=32768, top_k=kk), K.OP_ANCHOR_DECODE) for kk in (1024, 2048)}
+    assert short[2048] == short[1024]                              # one sub-segment: no candidates
     # anchor prefill holds the row lse and the ragged pooled scores
     tiles = -(-1000 // 128)
     ragged = 128 * (tiles - 1) * tiles // 2 + 1000
@@ -149,8 +155,9 @@ def test_shared_index_set_flag(L):
         assert L.validate(mk(shared_index_set=1), op) == K.OK
         assert L.validate(mk(shared_index_set=2), op) == K.ERR_INVALID
         assert L.validate(mk(shared_index_set=-1), op) == K.ERR_INVALID
+    # the shared decode anchor keeps one pooled row per batch row (B x N floats)
     assert L.workspace_bytes(_prob(shared_index_set=1), K.OP_ANCHOR_DECODE) == \
-        L.workspace_bytes(_prob(), K.OP_ANCHOR_DECODE)
+        L.workspace_bytes(_prob(), K.OP_ANCHOR_DECODE) + 2 * 4096 * 4
     ragged = 128 * 7 * 8 // 2 + 1000           # 8 tiles of 128 over N = 1000
     grow = L.workspace_bytes(_prefill(shared_index_set=1), K.OP_ANCHOR_PREFILL) - \
         L.workspace_bytes(_prefill(), K.OP_ANCHOR_PREFILL)
