@@ -102,16 +102,18 @@ DecodeWorkspace decode_workspace(const kascade_problem* p, int op) {
     off += align_up(rows * decode_logits_ld(p->kv_len) * sizeof(float));
     w.lse2 = off;
     off += align_up(rows * sizeof(float));
-    if (p->shared_index_set) {  // one pooled row per batch row
+    // Selection segments: one per (b, KV head), or one per batch row (shared set,
+    // whose pooled row is kept here); long segments need sub-segment candidates.
+    const size_t segments = (size_t)p->batch * (p->shared_index_set ? 1 : p->num_kv_heads);
+    if (p->shared_index_set) {
       w.pooled = off;
       off += align_up((size_t)p->batch * p->kv_len * sizeof(float));
-    } else {  // sub-segment candidates of long segments
-      const size_t cand = (size_t)p->batch * p->num_kv_heads * topk_decode_candidates(p->kv_len, p->top_k);
-      w.cand_val = off;
-      off += align_up(cand * sizeof(float));
-      w.cand_idx = off;
-      off += align_up(cand * sizeof(int32_t));
     }
+    const size_t cand = segments * topk_decode_candidates(p->kv_len, p->top_k);
+    w.cand_val = off;
+    off += align_up(cand * sizeof(float));
+    w.cand_idx = off;
+    off += align_up(cand * sizeof(int32_t));
   }
   w.total = off;
   return w;
@@ -306,7 +308,9 @@ int kascade_anchor_decode(const kascade_problem* p, const void* q, const void* k
   if (p->shared_index_set) {
     KASCADE_TRY("pool_all_heads", launch_pool_all_heads(a.logits, a.logits_ld, lse2, p->batch, a.hq,
                                                         a.n, pooled, s));
-    KASCADE_TRY("topk_rows", launch_topk_rows(pooled, p->batch, a.n, p->top_k, idx, s));
+    KASCADE_TRY("topk_rows", launch_topk_rows(pooled, p->batch, a.n, p->top_k,
+                                              reinterpret_cast<float*>(ws + w.cand_val),
+                                              reinterpret_cast<int32_t*>(ws + w.cand_idx), idx, s));
   } else {
     KASCADE_TRY("topk_decode", launch_topk_decode(a.logits, a.logits_ld, lse2, p->batch, a.hq, a.hkv,
                                                   a.group, a.n, p->top_k,

@@ -51,9 +51,11 @@ size_t topk_decode_candidates(int n, int k);
 hipError_t launch_topk_decode(const float* logits, int ld, const float* lse2, int batch, int hq,
                               int hkv, int group, int n, int k, float* cand_val, int32_t* cand_idx,
                               int32_t* idx, hipStream_t s);
-// Rows of n scores each, one selection per row: [rows, n] -> idx [rows, k].
-hipError_t launch_topk_rows(const float* scores, int rows, int n, int k, int32_t* idx,
-                            hipStream_t s);
+// Rows of n scores each, one selection per row: [rows, n] -> idx [rows, k];
+// rows longer than one sub-segment use candidate arrays of
+// topk_decode_candidates(n, k) entries per row.
+hipError_t launch_topk_rows(const float* scores, int rows, int n, int k, float* cand_val, int32_t* cand_idx,
+                            int32_t* idx, hipStream_t s);
 // Decode, one set for all heads: pooled[b][j] = sum over the Hq heads of
 // exp2(logit - lse2) from the logits [B*Hq, ld] and lse2 [B*Hq].
 hipError_t launch_pool_all_heads(const float* logits, int ld, const float* lse2, int batch, int hq,

@@ -383,6 +383,30 @@ __global__ __launch_bounds__(NT) void topk_merge_kernel(const float* cand_val, c
   }
 }
 
+// Rows of scores in memory longer than one sub-segment: workgroup
+// (row, sub) selects the exact top-k of keys [sub * kSub, ...) of its row into
+// the candidate arrays, laid out as for topk_decode_kernel.
+__global__ __launch_bounds__(kThreads) void topk_rows_sub_kernel(const float* scores, int n, int k, int nsub,
+                                                                   float* cand_val, int32_t* cand_idx) {
+  constexpr int NT = kThreads;
+  const int row = (int)blockIdx.x / nsub, sub = (int)blockIdx.x % nsub;
+  const int base = sub * kSub;
+  const int n_sub = min(kSub, n - base);
+  const float* src = scores + (size_t)row * n + base;
+  __shared__ unsigned staged[stage_len<NT>()];
+  unsigned u[kRegs];
+#pragma unroll
+  for (int i = 0; i < kRegs; ++i) {
+    const int j = key_of<NT>(i, threadIdx.x);
+    u[i] = j < n_sub ? __float_as_uint(src[j]) : 0u;
+    if (j < n_sub) staged[stage_index(j)] = u[i];
+  }
+  __syncthreads();
+  const size_t off = ((size_t)row * nsub + sub) * min(k, kSub);
+  const int kc = min(k, n_sub);
+  select_registers<NT>(u, staged, n_sub, kc, kc, CandOut{cand_idx + off, base, nullptr, cand_val + off});
+}
+
 // Tiles t0 + blockIdx.x of every (b, KV head); NT threads per segment.
 template <int NT>
 __global__ __launch_bounds__(NT) void topk_prefill_kernel(const float* pooled, int hkv, int n, int tile,
@@ -462,10 +486,28 @@ __global__ __launch_bounds__(kPoolThreads) void sum_sets_kernel(const float* poo
 
 }  // namespace
 
-hipError_t launch_topk_rows(const float* scores, int rows, int n, int k, int32_t* idx,
-                            hipStream_t s) {
-  // A row is a single prefill segment whose tile spans all n keys.
-  return launch_select_tiles(scores, rows, 1, n, n, (size_t)n, k, idx, s);
+static hipError_t launch_topk_merge(const float* cand_val, const int32_t* cand_idx, int segments, int n, int k,
+                                    int nsub, int32_t* idx, hipStream_t s) {
+  if (merge_candidates(n, k, nsub) <= kRegs * kSmallThreads)
+    hipLaunchKernelGGL(topk_merge_kernel<kSmallThreads>, dim3(segments), dim3(kSmallThreads), 0, s, cand_val,
+                       cand_idx, n, k, nsub, idx);
+  else
+    hipLaunchKernelGGL(topk_merge_kernel<kThreads>, dim3(segments), dim3(kThreads), 0, s, cand_val, cand_idx, n,
+                       k, nsub, idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_rows(const float* scores, int rows, int n, int k, float* cand_val, int32_t* cand_idx,
+                            int32_t* idx, hipStream_t s) {
+  const int nsub = topk_decode_subsegments(n);
+  // Up to one sub-segment a row is a single prefill segment whose tile spans
+  // all n keys; longer rows go through sub-segment candidates and a merge.
+  if (nsub == 1) return launch_select_tiles(scores, rows, 1, n, n, (size_t)n, k, idx, s);
+  hipLaunchKernelGGL(topk_rows_sub_kernel, dim3(rows * nsub), dim3(kThreads), 0, s, scores, n, k, nsub, cand_val,
+                     cand_idx);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_topk_merge(cand_val, cand_idx, rows, n, k, nsub, idx, s);
 }
 
 hipError_t launch_pool_all_heads(const float* logits, int ld, const float* lse2, int batch, int hq,
@@ -486,6 +528,7 @@ hipError_t launch_sum_sets(const float* pooled, int batch, int hkv, size_t len, 
 
 int topk_decode_subsegments(int n) { return (n + kSub - 1) / kSub; }
 
+
 size_t topk_decode_candidates(int n, int k) {
   const int nsub = topk_decode_subsegments(n);
   return nsub > 1 ? (size_t)nsub * (size_t)min(k, kSub) : 0;
@@ -503,13 +546,7 @@ hipError_t launch_topk_decode(const float* logits, int ld, const float* lse2, in
                        ld, lse2, hq, hkv, group, n, k, nsub, cand_val, cand_idx, idx);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsub == 1) return e;
-  if (merge_candidates(n, k, nsub) <= kRegs * kSmallThreads)
-    hipLaunchKernelGGL(topk_merge_kernel<kSmallThreads>, dim3(batch * hkv), dim3(kSmallThreads), 0, s, cand_val,
-                       cand_idx, n, k, nsub, idx);
-  else
-    hipLaunchKernelGGL(topk_merge_kernel<kThreads>, dim3(batch * hkv), dim3(kThreads), 0, s, cand_val, cand_idx,
-                       n, k, nsub, idx);
-  return hipGetLastError();
+  return launch_topk_merge(cand_val, cand_idx, batch * hkv, n, k, nsub, idx, s);
 }
 
 hipError_t launch_topk_prefill(const float* scores, int batch, int hkv, int n, int tile, int k,
