@@ -208,3 +208,39 @@ def test_graph_replay_matches_eager(lib):
         for n in outs:
             assert torch.equal(outs[n], ref[n]), n
         assert torch.equal(didx, ref_idx[0]) and torch.equal(pidx, ref_idx[1])
+
+
+# ---- selection across 32768-key sub-segments ----------------------------------
+
+@pytest.mark.parametrize("n,k", [(70000, 100), (70001, 40000)])
+def test_decode_ties_across_subsegments(lib, n, k):
+    """All keys identical over three sub-segments: the k lowest keys win,
+    including when k exceeds a sub-segment and the merge reads its
+    candidates from memory."""
+    log(f"[decode] case=ties_across_subsegments n={n} k={k}")
+    B, Hq, Hkv, d = 1, 2, 1, 64
+    g = torch.Generator().manual_seed(12)
+    q = torch.randn((B, Hq, 1, d), generator=g).to(torch.bfloat16)
+    row = torch.randn((1, 1, 1, d), generator=g).to(torch.bfloat16)
+    kk = row.expand(B, Hkv, n, d).contiguous()
+    idx = K.anchor_decode(q.to(DEV), kk.to(DEV), None, k)
+    torch.cuda.synchronize()
+    assert idx.cpu().numpy().reshape(-1).tolist() == list(range(k))
+
+
+@pytest.mark.parametrize("n,k", [(40000, 40000), (40000, 33000), (65537, 1000)])
+def test_decode_long_segments_against_oracle(lib, orc, n, k):
+    """Segments over one sub-segment: k = N keeps every key; k above a
+    sub-segment sends the merge through memory; a ragged last sub-segment of
+    one key."""
+    w = _small(f"long_{n}_{k}", wid=914, batch=1, hq=4, hkv=2, d=64, n=n, k=k, planted=32)
+    log(f"[decode] case=long_segments n={n} k={k}")
+    (q, kk, v), _ = _layers(w)
+    idx = K.anchor_decode(q.to(DEV), kk.to(DEV), None, k)
+    torch.cuda.synchronize()
+    gi = idx.cpu().numpy().reshape(-1, k)
+    io, po = orc.anchor_decode(to_oracle(q), to_oracle(kk), k)
+    for u in range(gi.shape[0]):
+        check_index_band(gi[u], io[u], po[u], k, n, f"long n={n} k={k} unit {u}")
+    if k == n:
+        assert np.array_equal(gi, np.tile(np.arange(n, dtype=np.int32), (gi.shape[0], 1)))
