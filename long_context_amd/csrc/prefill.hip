@@ -63,29 +63,87 @@ __device__ __forceinline__ lds_bf16x4 lds_read_transposed(const __bf16* p) {
 //   half hf stands for key 16ks + 8(j/4) + 4hf + (j%4); the A operand supplies
 //   V at those keys for d = 32db + l%32, two transposed LDS reads of four
 //   consecutive keys each.
+// Direct global -> LDS loads (16 or 4 bytes per lane; lane l of the wavefront
+// writes LDS bytes [lds + size*l, +size)). They are issued from inline
+// assembly so that the compiler does not wait for them before every LDS read
+// (it cannot tell the buffers apart); completion is awaited explicitly with
+// s_waitcnt vmcnt, see wait_vm.
+__device__ __forceinline__ void lds_dma16(const void* src, unsigned lds) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void lds_dma4(const void* src, unsigned lds) {
+  asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ unsigned lds_address(const void* p) { return (unsigned)(size_t)p; }
+
+// s_waitcnt vmcnt(n) for a run-time n (expcnt and lgkmcnt left unconstrained).
+__device__ __forceinline__ void wait_vm(int n) {
+#define KASCADE_VM(N) \
+  case N: __builtin_amdgcn_s_waitcnt(0x0F70 | ((N) & 15) | (((N) >> 4) << 14)); break;
+  switch (n) {
+    KASCADE_VM(0) KASCADE_VM(1) KASCADE_VM(2) KASCADE_VM(3) KASCADE_VM(4) KASCADE_VM(5) KASCADE_VM(6)
+    KASCADE_VM(7) KASCADE_VM(8) KASCADE_VM(9) KASCADE_VM(10) KASCADE_VM(11) KASCADE_VM(12) KASCADE_VM(13)
+    KASCADE_VM(14) KASCADE_VM(15) KASCADE_VM(16) KASCADE_VM(17) KASCADE_VM(18) KASCADE_VM(19)
+    KASCADE_VM(20) KASCADE_VM(21) KASCADE_VM(22) KASCADE_VM(23) KASCADE_VM(24) KASCADE_VM(25)
+    KASCADE_VM(26) KASCADE_VM(27) KASCADE_VM(28) KASCADE_VM(29) KASCADE_VM(30) KASCADE_VM(31)
+    KASCADE_VM(32) KASCADE_VM(33) KASCADE_VM(34) KASCADE_VM(35) KASCADE_VM(36) KASCADE_VM(37)
+    KASCADE_VM(38) KASCADE_VM(39) KASCADE_VM(40) KASCADE_VM(41) KASCADE_VM(42) KASCADE_VM(43)
+    KASCADE_VM(44) KASCADE_VM(45) KASCADE_VM(46) KASCADE_VM(47) KASCADE_VM(48) KASCADE_VM(49)
+    KASCADE_VM(50) KASCADE_VM(51) KASCADE_VM(52) KASCADE_VM(53) KASCADE_VM(54) KASCADE_VM(55)
+    KASCADE_VM(56) KASCADE_VM(57) KASCADE_VM(58) KASCADE_VM(59) KASCADE_VM(60) KASCADE_VM(61)
+    KASCADE_VM(62) KASCADE_VM(63)
+    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+  }
+#undef KASCADE_VM
+}
+
+// Staged rows are stored without padding; the 16-byte slot s of row r sits at
+// slot s ^ swz(r). Eight consecutive rows read at one slot (the K operand) and
+// the four rows of a transposed V read (slot pairs 2j, 2j+1) then fall on
+// distinct banks.
+__host__ __device__ constexpr int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
 // TR query rows per workgroup and head (the selection tile in gather mode;
-// kTile in the dense pass), TR / 32 wavefronts per head, NH heads.
-template <int D, bool GATHER, bool WITH_O, int NH, int KC, int TR>
+// kTile in the dense pass), TR / 32 wavefronts per head, NH heads, key chunks
+// of KC keys.
+//   Dense pass: the chunk's rows go straight from HBM into a ring of NB LDS
+//   buffers (unpadded rows, 16-byte slots swizzled), chunk c + NB - 1 loading
+//   while chunk c is used.
+//   Gather (reuse): rows go through registers into two padded LDS buffers,
+//   the list entries one chunk ahead of the rows; measured faster for the
+//   scattered rows than the direct loads.
+template <int D, bool GATHER, bool WITH_O, int NH, int KC, int TR, int NB>
 __global__ __launch_bounds__(64 * (TR / kRowsPerWave) * NH) void prefill_attn(PrefillArgs a) {
+  constexpr bool DMA = !GATHER;
   constexpr int kKeyChunk = KC;
-  constexpr int kKeyWaves = KC / 64;  // wavefronts that hold the chunk's list entries
+  constexpr int kKeyWaves = KC / 64;  // wavefronts that hold the chunk's list entries (gather)
   constexpr int C = D / 16;           // 16-element contraction chunks of S^T
   constexpr int DB = D / 32;          // 32-row blocks of O^T
-  constexpr int LD = D + kLdsPad;        // K rows: 16-byte operand reads spread over the banks
-  // V rows: a transposed read fetches four consecutive rows at 64 consecutive
-  // bytes (two 16-lane groups), so rows are padded by 64 bytes (16 banks):
-  // the four rows then cover all 64 banks.
+  constexpr int ROWB = D * 2;         // bytes per unpadded row
+  // Padded rows (register staging): K rows by 16 elements, so 16-byte operand
+  // reads spread over the banks; V rows by 32, since a transposed read fetches
+  // four consecutive rows at 64 consecutive bytes and 64 bytes of padding make
+  // the four rows cover all 64 banks.
+  constexpr int LD = D + kLdsPad;
   constexpr int LDV = D + 32;
   constexpr int WPH = TR / kRowsPerWave;                 // wavefronts per head
   constexpr int THREADS = 64 * WPH * NH;
+  constexpr int WAVES = THREADS / 64;
   constexpr int VPR = D / 8;                             // 16-byte vectors per row
-  constexpr int LPT = kKeyChunk * VPR / THREADS;         // vectors per thread per tensor
+  constexpr int LPT = kKeyChunk * VPR / THREADS;         // vectors per thread per tensor (registers)
   static_assert(LPT >= 1 && kKeyChunk * VPR % THREADS == 0, "chunk must split evenly");
-  __shared__ __attribute__((aligned(16))) __bf16 ks[2][kKeyChunk * LD];
-  __shared__ __attribute__((aligned(16))) __bf16 vs[WITH_O ? 2 : 1][WITH_O ? kKeyChunk * LDV : 8];
-  __shared__ int keys_s[2][kKeyChunk];
+  constexpr int NBUF = DMA ? NB : 2;
+  constexpr int KROW_BYTES = DMA ? ROWB : LD * 2;
+  constexpr int VROW_BYTES = DMA ? ROWB : LDV * 2;
+  constexpr int NI = KC * ROWB / 1024 / WAVES;           // 1-KB direct loads per wavefront and tensor
+  static_assert(!DMA || (NI >= 1 && KC * ROWB % (1024 * WAVES) == 0), "direct loads must split evenly");
+  static_assert(KC % 32 == 0 && (!GATHER || KC % 64 == 0) && NB >= 2, "staging shape");
+  constexpr int R = NI * (WITH_O ? 2 : 1);               // direct loads per wavefront and chunk
+  __shared__ __attribute__((aligned(1024))) unsigned char ks[NBUF][KC * KROW_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char vs[WITH_O ? NBUF : 1][WITH_O ? KC * VROW_BYTES : 16];
+  __shared__ int keys_s[GATHER ? 2 : 1][GATHER ? kKeyChunk : 1];
   // gather mode, per key-holding wavefront: smallest valid key, largest key, any padding
-  __shared__ int info_s[2][kKeyWaves][4];
+  __shared__ int info_s[GATHER ? 2 : 1][GATHER ? kKeyWaves : 1][4];
 
   // Longest tiles first across all heads and batches: workgroup i takes tile
   // tiles-1 - i / (B * Hq/NH) of TR rows, so the dispatcher hands out the work in
@@ -129,46 +187,43 @@ __global__ __launch_bounds__(64 * (TR / kRowsPerWave) * NH) void prefill_attn(Pr
 #pragma unroll
   for (int i = 0; i < DB; ++i) acc[i] = zero_f32x16();
 
-  // ---- staging: chunk c's rows go global -> registers -> LDS ----------------
-  bf16x8 kr[LPT], vr[LPT];
+  // ---- register staging (gather): global -> registers -> padded LDS ---------
+  bf16x8 kr[DMA ? 1 : LPT], vr[DMA ? 1 : LPT];
   int key_reg = -1;
   auto key_at = [&](int pos) __attribute__((always_inline)) {
     int key = pos < list_len ? (GATHER ? list[pos] : pos) : -1;
     return key < a.n ? key : -1;  // entries outside the sequence are skipped
   };
-  // Gather mode reads a chunk's list entries one fetch ahead (next_keys), so
-  // the row loads of a fetch never wait on the list.
-  int next_keys[LPT];
+  // The chunk's list entries are read one fetch ahead (next_keys), so the row
+  // loads of a fetch never wait on the list.
+  int next_keys[DMA ? 1 : LPT];
   int next_key_reg = -1;
   auto load_keys = [&](int c) __attribute__((always_inline)) {
-    if (GATHER) {
 #pragma unroll
-      for (int i = 0; i < LPT; ++i) next_keys[i] = key_at(c * kKeyChunk + (tid + i * THREADS) / VPR);
-      if (tid < kKeyChunk) next_key_reg = key_at(c * kKeyChunk + tid);
-    }
+    for (int i = 0; i < LPT; ++i) next_keys[i] = key_at(c * kKeyChunk + (tid + i * THREADS) / VPR);
+    if (tid < kKeyChunk) next_key_reg = key_at(c * kKeyChunk + tid);
   };
   auto fetch = [&](int c) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
       const int slot = tid + i * THREADS;
-      const int row = slot / VPR, colv = (slot % VPR) * 8;
-      const int key = GATHER ? next_keys[i] : key_at(c * kKeyChunk + row);
-      const size_t src = (size_t)(key < 0 ? 0 : key) * D + colv;
+      const int colv = (slot % VPR) * 8;
+      const size_t src = (size_t)(next_keys[i] < 0 ? 0 : next_keys[i]) * D + colv;
       kr[i] = load_bf16x8(kb + src);
       if (WITH_O) vr[i] = load_bf16x8(vb + src);
     }
-    if (GATHER && tid < kKeyChunk) key_reg = next_key_reg;
-    if (GATHER && (c + 1) * kKeyChunk < list_len) load_keys(c + 1);
+    if (tid < kKeyChunk) key_reg = next_key_reg;
+    if ((c + 1) * kKeyChunk < list_len) load_keys(c + 1);
   };
   auto stash = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
       const int slot = tid + i * THREADS;
       const int row = slot / VPR, colv = (slot % VPR) * 8;
-      *reinterpret_cast<bf16x8*>(&ks[buf][row * LD + colv]) = kr[i];
-      if (WITH_O) *reinterpret_cast<bf16x8*>(&vs[buf][row * LDV + colv]) = vr[i];
+      *reinterpret_cast<bf16x8*>(&ks[buf][(row * LD + colv) * 2]) = kr[i];
+      if (WITH_O) *reinterpret_cast<bf16x8*>(&vs[buf][(row * LDV + colv) * 2]) = vr[i];
     }
-    if (GATHER && wave < kKeyWaves) {  // these waves hold the chunk's keys, one per lane
+    if (wave < kKeyWaves) {  // these waves hold the chunk's keys, one per lane
       keys_s[buf][tid] = key_reg;
       int lo = key_reg >= 0 ? key_reg : 0x7fffffff, hi = key_reg;
 #pragma unroll
@@ -185,29 +240,60 @@ __global__ __launch_bounds__(64 * (TR / kRowsPerWave) * NH) void prefill_attn(Pr
     }
   };
 
+  // ---- direct staging (dense): chunk c into ring buffer c % NB ----------------
+  // This wavefront's NI 1-KB loads per tensor: lane l of load j fills row r,
+  // stored slot p, which holds slot p ^ swz(r) of key c * KC + r.
+  auto issue_rows = [&](int c) __attribute__((always_inline)) {
+    const int buf = c % NB;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int o = (wave * NI + j) * 1024 + 16 * lane;
+      const int r = o / ROWB, p = (o % ROWB) / 16;
+      const int key = c * kKeyChunk + r;
+      const size_t src = (size_t)(key < list_len ? key : 0) * D + 8 * (p ^ swz(r));
+      lds_dma16(kb + src, lds_address(&ks[buf][(wave * NI + j) * 1024]));
+      if constexpr (WITH_O) lds_dma16(vb + src, lds_address(&vs[buf][(wave * NI + j) * 1024]));
+    }
+  };
+
   // ---- one 32-key step of a staged chunk -------------------------------------
   // Operands come from LDS ahead of use: the K fragments of a step are read
   // before the previous step's P.V, and the V^T fragments of a step before its
   // softmax, so LDS latency hides behind matrix-core and ALU work.
+  // K operand: row 32sub + col, elements 16c + 8hf (swizzled: row % 8 = col % 8,
+  // slot 2c + hf).
+  const int kswz = swz(col & 7);
   auto read_k = [&](int buf, int sub, bf16x8 (&kf)[C]) __attribute__((always_inline)) {
-    const __bf16* krow = &ks[buf][(32 * sub + col) * LD + 8 * hf];
+    const unsigned char* krow = &ks[buf][(32 * sub + col) * KROW_BYTES];
 #pragma unroll
-    for (int c = 0; c < C; ++c) kf[c] = *reinterpret_cast<const bf16x8*>(krow + 16 * c);
+    for (int c = 0; c < C; ++c) {
+      const int off = DMA ? 16 * ((2 * c + hf) ^ kswz) : 32 * c + 16 * hf;
+      kf[c] = *reinterpret_cast<const bf16x8*>(krow + off);
+    }
   };
   // V^T operand of d block db and key step s2: lane group g = l/16 reads, for
   // d = 32db + 16(g%2) + (l%16), keys 16s2 + 4hf + 0..3 and 16s2 + 8 + 4hf + 0..3
-  // (row base + L/4, columns 4(L%4) of the lane's transposed read).
+  // (row base + L/4, columns 4(L%4) of the lane's transposed read). In the
+  // swizzled layout those rows have row % 8 = 4(g/2) + L/4, so the swizzle is a
+  // lane constant.
+  const int vL = lane & 15, vg = lane >> 4;
+  const int vrow = 4 * (vg >> 1) + (vL >> 2);
+  const int vswz = swz(vrow);
   auto read_v = [&](int buf, int sub, bf16x8 (&vf)[DB][2]) __attribute__((always_inline)) {
-    const int L = lane & 15, g = lane >> 4;
-    const __bf16* v0 = &vs[WITH_O ? buf : 0][(32 * sub + 4 * (g >> 1) + (L >> 2)) * LDV + 16 * (g & 1) + 4 * (L & 3)];
+    const unsigned char* v0 = &vs[WITH_O ? buf : 0][(32 * sub + vrow) * VROW_BYTES];
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db) {
+      const int off = DMA ? 16 * ((2 * (vg & 1) + ((vL & 3) >> 1) + 4 * db) ^ vswz) + 8 * (vL & 1)
+                          : 2 * (16 * (vg & 1) + 4 * (vL & 3) + 32 * db);
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        const lds_bf16x4 lo = lds_read_transposed(v0 + (16 * s2) * LDV + 32 * db);
-        const lds_bf16x4 hi = lds_read_transposed(v0 + (16 * s2 + 8) * LDV + 32 * db);
+        const lds_bf16x4 lo =
+            lds_read_transposed(reinterpret_cast<const __bf16*>(v0 + (16 * s2) * VROW_BYTES + off));
+        const lds_bf16x4 hi =
+            lds_read_transposed(reinterpret_cast<const __bf16*>(v0 + (16 * s2 + 8) * VROW_BYTES + off));
         vf[db][s2] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
+    }
   };
   auto step = [&](int buf, int c, int sub, bool masked, bf16x8 (&kf)[C]) __attribute__((always_inline)) {
     bf16x8 vf[DB][2];
@@ -274,42 +360,73 @@ __global__ __launch_bounds__(64 * (TR / kRowsPerWave) * NH) void prefill_attn(Pr
     for (int sub = 0; sub < KC / 32; ++sub) step(buf, c, sub, masked, kf);
   };
 
-  // list_len >= 1 (k >= 1 and prefix_t >= 1), so chunk 0 always exists.
-  load_keys(0);
-  fetch(0);
-  stash(0);
-  // Complete the Q operand loads here: a wait for them inside the loop would
-  // also wait for the prefetch of the next chunk (vector-memory counts retire
-  // in order). s_waitcnt vmcnt(0), other counters unconstrained.
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  __syncthreads();
-  if (nchunks > 1) fetch(1);
-  for (int c = 0; c < nchunks; ++c) {
-    const int buf = c & 1;
-    if (wrow0 < a.n) {
-      int vmin, vmax;
-      bool pad;
-      if (GATHER) {
-        vmin = info_s[buf][0][0];
-        vmax = info_s[buf][0][1];
-        pad = info_s[buf][0][2] != 0;
+  if constexpr (DMA) {
+    // Per wavefront the direct loads are counted as issued; before chunk c is
+    // used, s_waitcnt vmcnt(issued - rows_q[0]) leaves only later chunks' loads
+    // in flight. rows_q[i] is the count right after chunk c + i's loads.
+    // Chunks past the end issue no loads, so the count is tracked rather than
+    // assumed. The Q operand loads complete at the first vmcnt(0).
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    int issued = 0;
+    int rows_q[NB - 1];
+#pragma unroll
+    for (int c = 0; c < NB - 1; ++c) {
+      if (c < nchunks) {
+        issue_rows(c);
+        issued += R;
+      }
+      rows_q[c] = issued;
+    }
+    for (int c = 0; c < nchunks; ++c) {
+      const int buf = c % NB;
+      wait_vm(issued - rows_q[0]);
+      __syncthreads();  // chunk c is in place; chunk c - 1's buffer is released
+      const int nc = c + NB - 1;
+      if (nc < nchunks) {
+        issue_rows(nc);
+        issued += R;
+      }
+#pragma unroll
+      for (int i = 0; i + 1 < NB - 1; ++i) rows_q[i] = rows_q[i + 1];
+      rows_q[NB - 2] = issued;
+      if (wrow0 < a.n) {
+        const int vmin = c * kKeyChunk;
+        const int vmax = min(vmin + kKeyChunk, list_len) - 1;
+        const bool pad = vmin + kKeyChunk > list_len;
+        if (vmin <= wrow_last)  // otherwise every key is above every row of the wave
+          chunk_step(buf, c, pad || vmax > wrow0);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // no load left in flight at exit
+  } else {
+    // list_len >= 1 (k >= 1 and prefix_t >= 1), so chunk 0 always exists.
+    load_keys(0);
+    fetch(0);
+    stash(0);
+    // Complete the Q operand loads here: a wait for them inside the loop would
+    // also wait for the prefetch of the next chunk (vector-memory counts retire
+    // in order). s_waitcnt vmcnt(0), other counters unconstrained.
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (nchunks > 1) fetch(1);
+    for (int c = 0; c < nchunks; ++c) {
+      const int buf = c & 1;
+      if (wrow0 < a.n) {
+        int vmin = info_s[buf][0][0], vmax = info_s[buf][0][1];
+        bool pad = info_s[buf][0][2] != 0;
 #pragma unroll
         for (int w = 1; w < kKeyWaves; ++w) {
           vmin = min(vmin, info_s[buf][w][0]);
           vmax = max(vmax, info_s[buf][w][1]);
           pad = pad || info_s[buf][w][2] != 0;
         }
-      } else {
-        vmin = c * kKeyChunk;
-        vmax = min(vmin + kKeyChunk, list_len) - 1;
-        pad = vmin + kKeyChunk > list_len;
+        if (vmin <= wrow_last)  // otherwise every key is above every row of the wave
+          chunk_step(buf, c, pad || vmax > wrow0);
       }
-      if (vmin <= wrow_last)  // otherwise every key is above every row of the wave
-        chunk_step(buf, c, pad || vmax > wrow0);
+      if (c + 1 < nchunks) stash(buf ^ 1);  // that buffer was released at the last barrier
+      __syncthreads();
+      if (c + 2 < nchunks) fetch(c + 2);
     }
-    if (c + 1 < nchunks) stash(buf ^ 1);  // that buffer was released at the last barrier
-    __syncthreads();
-    if (c + 2 < nchunks) fetch(c + 2);
   }
 
   // Row totals: each lane half summed its own keys.
@@ -525,20 +642,20 @@ hipError_t launch_attn(const PrefillArgs& a, hipStream_t s) {
   // Reuse layers: the heads of a GQA group that fill eight wavefronts (two
   // heads of 128 rows, or four of 64) share every gathered K/V chunk, staged
   // 128 keys at a time so each gather has a long step of work to land behind.
-  // Dense pass: one head per workgroup and 64-key steps, two workgroups per
-  // compute unit.
+  // Dense pass: one head per workgroup, 64-key chunks in a ring of two
+  // buffers, two workgroups per compute unit.
   constexpr int WPH = TR / kRowsPerWave;
   constexpr int NHG = 8 / WPH;
   const int wtiles = (a.n + TR - 1) / TR;
   if (GATHER && a.group % NHG == 0) {
     dim3 grid(wtiles * a.batch * (a.hq / NHG));
-    hipLaunchKernelGGL((prefill_attn<D, GATHER, WITH_O, NHG, 128, TR>), grid, dim3(64 * WPH * NHG), 0, s, a);
+    hipLaunchKernelGGL((prefill_attn<D, GATHER, WITH_O, NHG, 128, TR, 2>), grid, dim3(64 * WPH * NHG), 0, s, a);
   } else if (GATHER && NHG > 2 && a.group % 2 == 0) {
     dim3 grid(wtiles * a.batch * (a.hq / 2));
-    hipLaunchKernelGGL((prefill_attn<D, GATHER, WITH_O, 2, 64, TR>), grid, dim3(64 * WPH * 2), 0, s, a);
+    hipLaunchKernelGGL((prefill_attn<D, GATHER, WITH_O, 2, 64, TR, 2>), grid, dim3(64 * WPH * 2), 0, s, a);
   } else {
     dim3 grid(wtiles * a.batch * a.hq);
-    hipLaunchKernelGGL((prefill_attn<D, GATHER, WITH_O, 1, 64, TR>), grid, dim3(64 * WPH), 0, s, a);
+    hipLaunchKernelGGL((prefill_attn<D, GATHER, WITH_O, 1, 64, TR, 2>), grid, dim3(64 * WPH), 0, s, a);
   }
   return hipGetLastError();
 }
