@@ -63,16 +63,18 @@ __device__ __forceinline__ lds_bf16x4 lds_read_transposed(const __bf16* p) {
 //   half hf stands for key 16ks + 8(j/4) + 4hf + (j%4); the A operand supplies
 //   V at those keys for d = 32db + l%32, two transposed LDS reads of four
 //   consecutive keys each.
-// Direct global -> LDS loads (16 or 4 bytes per lane; lane l of the wavefront
-// writes LDS bytes [lds + size*l, +size)). They are issued from inline
-// assembly so that the compiler does not wait for them before every LDS read
-// (it cannot tell the buffers apart); completion is awaited explicitly with
-// s_waitcnt vmcnt, see wait_vm.
+// Direct global -> LDS loads (16 bytes per lane; lane l of the wavefront
+// writes LDS bytes [lds + 16 l, +16)). They are issued from inline assembly so
+// that the compiler does not wait for them before every LDS read (it cannot
+// tell the buffers apart); completion is awaited explicitly with s_waitcnt
+// vmcnt, see wait_vm. lds_dma16 takes a per-lane address; lds_dma16_at a
+// wave-uniform base in scalar registers plus a per-lane 32-bit byte offset,
+// which costs no vector ALU work per load.
 __device__ __forceinline__ void lds_dma16(const void* src, unsigned lds) {
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
 }
-__device__ __forceinline__ void lds_dma4(const void* src, unsigned lds) {
-  asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+__device__ __forceinline__ void lds_dma16_at(const void* base, unsigned offset, unsigned lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(offset), "s"(base), "{m0}"(lds) : "memory");
 }
 __device__ __forceinline__ unsigned lds_address(const void* p) { return (unsigned)(size_t)p; }
 
@@ -97,11 +99,24 @@ __device__ __forceinline__ void wait_vm(int n) {
 #undef KASCADE_VM
 }
 
-// Staged rows are stored without padding; the 16-byte slot s of row r sits at
-// slot s ^ swz(r). Eight consecutive rows read at one slot (the K operand) and
-// the four rows of a transposed V read (slot pairs 2j, 2j+1) then fall on
-// distinct banks.
-__host__ __device__ constexpr int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// LDS banks: 64 of four bytes, so 256 bytes are one bank sweep. A 16-byte read
+// is served sixteen lanes at a time (lanes 16j..16j+15), an 8-byte transposed
+// read thirty-two lanes at a time; a read runs at full rate when each such
+// group covers distinct banks. The operand reads of prefill_attn are
+//   K (16 bytes, lane l: row 32 sub + l % 32, slot 2c + l / 32): sixteen
+//   consecutive rows at one slot;
+//   V^T (8 bytes transposed, per lane half): four consecutive rows, aligned
+//   to four, each at the four consecutive slots 4db + 0..3.
+// Direct loads fill unpadded rows, so there the 16-byte slot s of row r sits
+// at slot s ^ swz<D>(r). D = 128: the row bits (r1, r0, r2, r3), high to low,
+// whose top two bits tell four consecutive rows apart. D = 64 (rows r and
+// r ^ 1 share a bank sweep): the bit reversal of (r >> 1) & 7, whose top bit
+// tells rows two apart.
+template <int D>
+__host__ __device__ constexpr int swz(int r) {
+  return D == 128 ? (((r & 3) << 2) | (((r >> 2) & 1) << 1) | ((r >> 3) & 1))
+                  : ((((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 1) | ((r >> 3) & 1));
+}
 
 // TR query rows per workgroup and head (the selection tile in gather mode;
 // kTile in the dense pass), TR / 32 wavefronts per head, NH heads, key chunks
@@ -109,9 +124,12 @@ __host__ __device__ constexpr int swz(int r) { return ((r & 3) << 1) | ((r >> 2)
 //   Dense pass: the chunk's rows go straight from HBM into a ring of NB LDS
 //   buffers (unpadded rows, 16-byte slots swizzled), chunk c + NB - 1 loading
 //   while chunk c is used.
-//   Gather (reuse): rows go through registers into two padded LDS buffers,
-//   the list entries one chunk ahead of the rows; measured faster for the
-//   scattered rows than the direct loads.
+//   Gather (reuse): rows go through registers into two LDS buffers, the list
+//   entries one chunk ahead of the rows; measured faster for the scattered
+//   rows than the direct loads. These rows are padded instead of swizzled,
+//   which keeps every operand offset a compile-time constant: K rows by 8
+//   elements (an odd number of 16-byte slots per row), V rows by 32 (four
+//   consecutive rows start 64 bytes apart modulo a bank sweep).
 template <int D, bool GATHER, bool WITH_O, int NH, int KC, int TR, int NB>
 __global__ __launch_bounds__(64 * (TR / kRowsPerWave) * NH) void prefill_attn(PrefillArgs a) {
   constexpr bool DMA = !GATHER;
@@ -120,12 +138,6 @@ __global__ __launch_bounds__(64 * (TR / kRowsPerWave) * NH) void prefill_attn(Pr
   constexpr int C = D / 16;           // 16-element contraction chunks of S^T
   constexpr int DB = D / 32;          // 32-row blocks of O^T
   constexpr int ROWB = D * 2;         // bytes per unpadded row
-  // Padded rows (register staging): K rows by 16 elements, so 16-byte operand
-  // reads spread over the banks; V rows by 32, since a transposed read fetches
-  // four consecutive rows at 64 consecutive bytes and 64 bytes of padding make
-  // the four rows cover all 64 banks.
-  constexpr int LD = D + kLdsPad;
-  constexpr int LDV = D + 32;
   constexpr int WPH = TR / kRowsPerWave;                 // wavefronts per head
   constexpr int THREADS = 64 * WPH * NH;
   constexpr int WAVES = THREADS / 64;
@@ -133,8 +145,8 @@ __global__ __launch_bounds__(64 * (TR / kRowsPerWave) * NH) void prefill_attn(Pr
   constexpr int LPT = kKeyChunk * VPR / THREADS;         // vectors per thread per tensor (registers)
   static_assert(LPT >= 1 && kKeyChunk * VPR % THREADS == 0, "chunk must split evenly");
   constexpr int NBUF = DMA ? NB : 2;
-  constexpr int KROW_BYTES = DMA ? ROWB : LD * 2;
-  constexpr int VROW_BYTES = DMA ? ROWB : LDV * 2;
+  constexpr int KROW_BYTES = DMA ? ROWB : (D + 8) * 2;
+  constexpr int VROW_BYTES = DMA ? ROWB : (D + 32) * 2;
   constexpr int NI = KC * ROWB / 1024 / WAVES;           // 1-KB direct loads per wavefront and tensor
   static_assert(!DMA || (NI >= 1 && KC * ROWB % (1024 * WAVES) == 0), "direct loads must split evenly");
   static_assert(KC % 32 == 0 && (!GATHER || KC % 64 == 0) && NB >= 2, "staging shape");
@@ -219,9 +231,9 @@ __global__ __launch_bounds__(64 * (TR / kRowsPerWave) * NH) void prefill_attn(Pr
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
       const int slot = tid + i * THREADS;
-      const int row = slot / VPR, colv = (slot % VPR) * 8;
-      *reinterpret_cast<bf16x8*>(&ks[buf][(row * LD + colv) * 2]) = kr[i];
-      if (WITH_O) *reinterpret_cast<bf16x8*>(&vs[buf][(row * LDV + colv) * 2]) = vr[i];
+      const int row = slot / VPR, vec = slot % VPR;
+      *reinterpret_cast<bf16x8*>(&ks[buf][row * KROW_BYTES + 16 * vec]) = kr[i];
+      if (WITH_O) *reinterpret_cast<bf16x8*>(&vs[buf][row * VROW_BYTES + 16 * vec]) = vr[i];
     }
     if (wave < kKeyWaves) {  // these waves hold the chunk's keys, one per lane
       keys_s[buf][tid] = key_reg;
@@ -242,17 +254,37 @@ __global__ __launch_bounds__(64 * (TR / kRowsPerWave) * NH) void prefill_attn(Pr
 
   // ---- direct staging (dense): chunk c into ring buffer c % NB ----------------
   // This wavefront's NI 1-KB loads per tensor: lane l of load j fills row r,
-  // stored slot p, which holds slot p ^ swz(r) of key c * KC + r.
+  // stored slot p, which holds slot p ^ swz<D>(r) of key c * KC + r.
+  // A chunk whose rows all exist in the sequence loads from the chunk's first
+  // row (a scalar base) at lane-constant offsets; only a chunk running past
+  // the last row computes per-lane addresses, with those rows replaced by row 0.
+  unsigned dma_off[DMA ? NI : 1];
+#pragma unroll
+  for (int j = 0; j < (DMA ? NI : 1); ++j) {
+    const int o = (wave * NI + j) * 1024 + 16 * lane;
+    const int r = o / ROWB, p = (o % ROWB) / 16;
+    dma_off[j] = (unsigned)(r * D + 8 * (p ^ swz<D>(r))) * 2u;
+  }
   auto issue_rows = [&](int c) __attribute__((always_inline)) {
     const int buf = c % NB;
+    if ((c + 1) * kKeyChunk <= a.n) {
+      const u16* kc = kb + (size_t)c * kKeyChunk * D;
+      const u16* vc = vb + (size_t)c * kKeyChunk * D;
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const int o = (wave * NI + j) * 1024 + 16 * lane;
-      const int r = o / ROWB, p = (o % ROWB) / 16;
-      const int key = c * kKeyChunk + r;
-      const size_t src = (size_t)(key < list_len ? key : 0) * D + 8 * (p ^ swz(r));
-      lds_dma16(kb + src, lds_address(&ks[buf][(wave * NI + j) * 1024]));
-      if constexpr (WITH_O) lds_dma16(vb + src, lds_address(&vs[buf][(wave * NI + j) * 1024]));
+      for (int j = 0; j < NI; ++j) {
+        lds_dma16_at(kc, dma_off[j], lds_address(&ks[buf][(wave * NI + j) * 1024]));
+        if constexpr (WITH_O) lds_dma16_at(vc, dma_off[j], lds_address(&vs[buf][(wave * NI + j) * 1024]));
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        const int o = (wave * NI + j) * 1024 + 16 * lane;
+        const int r = o / ROWB, p = (o % ROWB) / 16;
+        const int key = c * kKeyChunk + r;
+        const size_t src = (size_t)(key < a.n ? key : 0) * D + 8 * (p ^ swz<D>(r));
+        lds_dma16(kb + src, lds_address(&ks[buf][(wave * NI + j) * 1024]));
+        if constexpr (WITH_O) lds_dma16(vb + src, lds_address(&vs[buf][(wave * NI + j) * 1024]));
+      }
     }
   };
 
@@ -260,9 +292,9 @@ __global__ __launch_bounds__(64 * (TR / kRowsPerWave) * NH) void prefill_attn(Pr
   // Operands come from LDS ahead of use: the K fragments of a step are read
   // before the previous step's P.V, and the V^T fragments of a step before its
   // softmax, so LDS latency hides behind matrix-core and ALU work.
-  // K operand: row 32sub + col, elements 16c + 8hf (swizzled: row % 8 = col % 8,
-  // slot 2c + hf).
-  const int kswz = swz(col & 7);
+  // K operand: row 32sub + col, elements 16c + 8hf (slot 2c + hf; the swizzle
+  // of the direct-load layout depends on row % 16 = col % 16).
+  const int kswz = swz<D>(col & 15);
   auto read_k = [&](int buf, int sub, bf16x8 (&kf)[C]) __attribute__((always_inline)) {
     const unsigned char* krow = &ks[buf][(32 * sub + col) * KROW_BYTES];
 #pragma unroll
@@ -273,24 +305,25 @@ __global__ __launch_bounds__(64 * (TR / kRowsPerWave) * NH) void prefill_attn(Pr
   };
   // V^T operand of d block db and key step s2: lane group g = l/16 reads, for
   // d = 32db + 16(g%2) + (l%16), keys 16s2 + 4hf + 0..3 and 16s2 + 8 + 4hf + 0..3
-  // (row base + L/4, columns 4(L%4) of the lane's transposed read). In the
-  // swizzled layout those rows have row % 8 = 4(g/2) + L/4, so the swizzle is a
-  // lane constant.
+  // (row base + L/4, columns 4(L%4) of the lane's transposed read). Those rows
+  // have row % 16 = 4(g/2) + L/4 for the first read and 8 more for the second,
+  // so each read's swizzle is a lane constant.
   const int vL = lane & 15, vg = lane >> 4;
   const int vrow = 4 * (vg >> 1) + (vL >> 2);
-  const int vswz = swz(vrow);
+  const int vslot = 2 * (vg & 1) + ((vL & 3) >> 1);
+  const int vswz0 = swz<D>(vrow), vswz1 = swz<D>(vrow + 8);
   auto read_v = [&](int buf, int sub, bf16x8 (&vf)[DB][2]) __attribute__((always_inline)) {
     const unsigned char* v0 = &vs[WITH_O ? buf : 0][(32 * sub + vrow) * VROW_BYTES];
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const int off = DMA ? 16 * ((2 * (vg & 1) + ((vL & 3) >> 1) + 4 * db) ^ vswz) + 8 * (vL & 1)
-                          : 2 * (16 * (vg & 1) + 4 * (vL & 3) + 32 * db);
+      const int off0 = DMA ? 16 * ((vslot + 4 * db) ^ vswz0) + 8 * (vL & 1) : 16 * (vslot + 4 * db) + 8 * (vL & 1);
+      const int off1 = DMA ? 16 * ((vslot + 4 * db) ^ vswz1) + 8 * (vL & 1) : off0;
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         const lds_bf16x4 lo =
-            lds_read_transposed(reinterpret_cast<const __bf16*>(v0 + (16 * s2) * VROW_BYTES + off));
+            lds_read_transposed(reinterpret_cast<const __bf16*>(v0 + (16 * s2) * VROW_BYTES + off0));
         const lds_bf16x4 hi =
-            lds_read_transposed(reinterpret_cast<const __bf16*>(v0 + (16 * s2 + 8) * VROW_BYTES + off));
+            lds_read_transposed(reinterpret_cast<const __bf16*>(v0 + (16 * s2 + 8) * VROW_BYTES + off1));
         vf[db][s2] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
     }
