@@ -151,6 +151,14 @@ using PlainOut = SelectOut<false, false>;   // positions are the keys
 using CandOut = SelectOut<false, true>;     // keys offset by key_base, scores kept
 using RemapOut = SelectOut<true, false>;    // keys looked up from a table
 
+// Selection key of a score: its float bit pattern with the sign bit cleared.
+// Pooled scores are sums of probabilities, hence non-negative, and their
+// patterns order like their values. Clearing the sign keeps every key below
+// 2^31 whatever the inputs were (a NaN of either sign included), which the
+// radix passes (bits 30..0) rely on to select exactly k keys.
+__device__ __forceinline__ unsigned score_key(float v) { return __float_as_uint(v) & 0x7fffffffu; }
+__device__ __forceinline__ unsigned score_key(unsigned bits) { return bits & 0x7fffffffu; }
+
 // Selection over a segment read from memory (any length).
 template <int NT, class Out>
 __device__ __forceinline__ void select_segment(const unsigned* keys, int n, int kt, int k, Out so) {
@@ -162,7 +170,7 @@ __device__ __forceinline__ void select_segment(const unsigned* keys, int n, int 
 
   if (kt >= n) {  // every candidate is kept
     for (int s = tid; s < k; s += NT) {
-      if (s < n) so.put(s, s, keys[s]);
+      if (s < n) so.put(s, s, score_key(keys[s]));
       else out[s] = -1;
     }
     return;
@@ -177,7 +185,7 @@ __device__ __forceinline__ void select_segment(const unsigned* keys, int n, int 
     __syncthreads();
     for (int j0 = 0; j0 < n; j0 += NT) {
       const int j = j0 + tid;
-      const unsigned u = j < n ? keys[j] : 0u;
+      const unsigned u = j < n ? score_key(keys[j]) : 0u;
       const bool match = j < n && (u & mask) == prefix;
       hist_add(hist, (u >> shift) & dmask, match);
     }
@@ -190,7 +198,7 @@ __device__ __forceinline__ void select_segment(const unsigned* keys, int n, int 
   unsigned base = 0, eq_seen = 0;
   for (int j0 = 0; j0 < n; j0 += NT) {
     const int j = j0 + tid;
-    const unsigned u = j < n ? keys[j] : 0u;
+    const unsigned u = j < n ? score_key(keys[j]) : 0u;
     const bool gt = j < n && u > prefix;
     const bool eq = j < n && u == prefix;
     unsigned eq_total;
@@ -335,7 +343,7 @@ __global__ __launch_bounds__(kDecodeThreads) void topk_decode_kernel(const float
 #pragma unroll
   for (int i = 0; i < kRegs; ++i) {
     const int j = key_of<NT>(i, tid);
-    u[i] = j < n_sub ? __float_as_uint(p[i]) : 0u;
+    u[i] = j < n_sub ? score_key(p[i]) : 0u;
     if (j < n_sub) staged[stage_index(j)] = u[i];
   }
   __syncthreads();
@@ -373,7 +381,7 @@ __global__ __launch_bounds__(NT) void topk_merge_kernel(const float* cand_val, c
 #pragma unroll
     for (int i = 0; i < kRegs; ++i) {
       const int j = key_of<NT>(i, threadIdx.x);
-      u[i] = j < m ? __float_as_uint(vals[j]) : 0u;
+      u[i] = j < m ? score_key(vals[j]) : 0u;
       if (j < m) staged[stage_index(j)] = u[i];
     }
     __syncthreads();
@@ -398,7 +406,7 @@ __global__ __launch_bounds__(kThreads) void topk_rows_sub_kernel(const float* sc
 #pragma unroll
   for (int i = 0; i < kRegs; ++i) {
     const int j = key_of<NT>(i, threadIdx.x);
-    u[i] = j < n_sub ? __float_as_uint(src[j]) : 0u;
+    u[i] = j < n_sub ? score_key(src[j]) : 0u;
     if (j < n_sub) staged[stage_index(j)] = u[i];
   }
   __syncthreads();
@@ -423,7 +431,7 @@ __global__ __launch_bounds__(NT) void topk_prefill_kernel(const float* pooled, i
 #pragma unroll
     for (int i = 0; i < kRegs; ++i) {
       const int j = key_of<NT>(i, threadIdx.x);
-      u[i] = j < prefix ? __float_as_uint(src[j]) : 0u;
+      u[i] = j < prefix ? score_key(src[j]) : 0u;
       if (j < prefix) staged[stage_index(j)] = u[i];
     }
     __syncthreads();
