@@ -135,6 +135,47 @@ __global__ __launch_bounds__(256) void decode_attn_bf16(DecodeArgs a) {
 #pragma unroll
   for (int i = 0; i < D / 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Dense mode keeps the scores of up to `cap` chunks in LDS, each lane its
+  // own values, and writes them out together after the last of them: logit
+  // stores interleaved with the sweep's loads cost more than the same stores
+  // issued in one burst per wavefront.
+  constexpr bool kBuffered = LOGITS && !GATHER;
+  // Per wavefront 16 KB (8 KB without P.V, 4 KB at d = 64), sized so that
+  // the buffers never limit how many wavefronts a compute unit holds.
+  constexpr int kLogitFloats = D == 128 ? (WITH_PV ? 4096 : 2048) : 1024;
+  __shared__ __attribute__((aligned(16))) float logit_buf[kBuffered ? kWavesPerBlock : 1][kBuffered ? kLogitFloats : 4];
+  float* lbuf = &logit_buf[kBuffered ? wave_id() : 0][0];
+  const int cap = kBuffered ? kLogitFloats / (32 * G) : 1;  // >= 2 chunks for G <= 16
+  int filled = 0;
+  auto store_logits = [&](float* dst, const f32x4& v, uint32_t valid, int e0) __attribute__((always_inline)) {
+    if ((valid >> (e0 + 3)) & 1u) {
+      *reinterpret_cast<f32x4*>(dst) = v;
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if ((valid >> (e0 + r)) & 1u) dst[r] = v[r];
+    }
+  };
+  // After chunk ci: write the buffered chunks out once the buffer is full or
+  // the sweep is done.
+  auto after_chunk = [&](int ci) __attribute__((always_inline)) {
+    if (!kBuffered) return;
+    if (++filled < cap && ci + 1 < nchunk) return;
+    if (n < G) {
+      for (int f = 0; f < filled; ++f) {
+        const int j0 = begin + stride * (ci - filled + 1 + f);
+        const int left = end - j0;
+        const uint32_t valid = left >= 32 ? 0xffffffffu : ((1u << left) - 1u);
+        float* row = a.logits + (size_t)(b * a.hq + h0 + n) * a.logits_ld + j0 + 4 * qg;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          store_logits(row + 16 * t, *reinterpret_cast<const f32x4*>(lbuf + (f * G + n) * 32 + 16 * t + 4 * qg),
+                       valid, 16 * t + 4 * qg);
+      }
+    }
+    filled = 0;
+  };
+
   auto compute = [&](DecodeStage<C>& st, int j0) __attribute__((always_inline)) {
     float x[2][4];
     float cmax = kNegBig;
@@ -150,14 +191,12 @@ __global__ __launch_bounds__(256) void decode_attn_bf16(DecodeArgs a) {
         cmax = fmaxf(cmax, x[t][r]);
       }
       if (LOGITS && n < G) {
-        float* dst = a.logits + (size_t)(b * a.hq + h0 + n) * a.logits_ld + j0 + 16 * t + 4 * qg;
-        if ((st.valid >> (16 * t + 4 * qg + 3)) & 1u) {
-          *reinterpret_cast<f32x4*>(dst) = f32x4{x[t][0], x[t][1], x[t][2], x[t][3]};
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if ((st.valid >> (16 * t + 4 * qg + r)) & 1u) dst[r] = x[t][r];
-        }
+        const f32x4 v = {x[t][0], x[t][1], x[t][2], x[t][3]};
+        if (kBuffered)
+          *reinterpret_cast<f32x4*>(lbuf + (filled * G + n) * 32 + 16 * t + 4 * qg) = v;
+        else
+          store_logits(a.logits + (size_t)(b * a.hq + h0 + n) * a.logits_ld + j0 + 16 * t + 4 * qg, v,
+                       st.valid, 16 * t + 4 * qg);
       }
     }
     cmax = group4_max(cmax);
@@ -220,6 +259,7 @@ __global__ __launch_bounds__(256) void decode_attn_bf16(DecodeArgs a) {
       const int j0 = begin + stride * i;
       load_stage(s0, entry_key(j0), j0);
       compute(s0, j0);
+      after_chunk(i);
     }
   } else {
   // Two chunks in flight: chunk i+1's rows are requested (and chunk i+2's
@@ -234,12 +274,14 @@ __global__ __launch_bounds__(256) void decode_attn_bf16(DecodeArgs a) {
       kn = entry_key(j0 + 2 * stride);
     }
     compute(s0, j0);
+    after_chunk(i);
     if (i + 1 >= nchunk) break;
     if (i + 2 < nchunk) {
       load_stage(s0, kn, j0 + 2 * stride);
       kn = entry_key(j0 + 3 * stride);
     }
     compute(s1, j0 + stride);
+    after_chunk(i + 1);
   }
   }
 
