@@ -550,14 +550,18 @@ __global__ __launch_bounds__(64 * kPoolWaves) void prefill_pool(PrefillArgs a, i
   // One step stages the tile's rows of one head of the group.
   bf16x8 qr[LPT];
   float lr = INFINITY;
+  // Rows are addressed from the tile's first row (a wave-uniform base) with
+  // 32-bit byte offsets below TP * D * 2; rows past N repeat row N - 1.
+  const int last_row = a.n - 1 - row0;
   auto fetch = [&](int step) __attribute__((always_inline)) {
     const int h = kvh * a.group + step;
-    const u16* qh = a.q + (size_t)(b * a.hq + h) * a.n * D;
+    const unsigned char* qt =
+        reinterpret_cast<const unsigned char*>(a.q + ((size_t)(b * a.hq + h) * a.n + row0) * D);
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
       const int slot = tid + i * THREADS;
       const int row = slot / VPR, col = (slot % VPR) * 8;
-      qr[i] = load_bf16x8(qh + (size_t)min(row0 + row, a.n - 1) * D + col);
+      qr[i] = *reinterpret_cast<const bf16x8*>(qt + (unsigned)(min(row, last_row) * D + col) * 2u);
     }
     if (tid < TP) {
       const int row = row0 + tid;
