@@ -56,6 +56,11 @@
  * Errors: each call returns a kascade_status. Argument errors are reported
  * before anything is enqueued. Device faults surface at the caller's next
  * synchronisation. Nothing is thrown across the ABI.
+ *
+ * Values: Q, K and V are expected to be finite. With NaN or infinite inputs
+ * the scores and outputs are undefined, but every index set an anchor call
+ * writes is still well formed (exactly min(k, candidates) distinct keys in
+ * range, ascending, then -1), so reuse calls stay in bounds.
  */
 #ifndef KASCADE_H
 #define KASCADE_H
