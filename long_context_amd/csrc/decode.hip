@@ -35,25 +35,31 @@ constexpr int kWavesPerBlock = 4;
 constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (log2 units)
 
 // Registers of one 32-key chunk in flight: K and V rows as A operands and the
-// validity of the chunk's 32 list entries (bit e = entry e usable).
-#ifndef KASCADE_DECODE_V_LATE
-#define KASCADE_DECODE_V_LATE 0
-#endif
-// V rows are requested after the scores of their chunk are computed, into the
-// registers K used, so that more wavefronts fit per SIMD.
-constexpr bool kVLate = KASCADE_DECODE_V_LATE != 0;
-
-template <int C>
+// validity of the chunk's 32 list entries (bit e = entry e usable). With
+// VLATE the V rows are requested after the chunk's scores are computed, into
+// the registers K used.
+template <int C, bool VLATE>
 struct DecodeStage {
   bf16x8 k[2][C];
-  bf16x8 v[2][kVLate ? 1 : C];
+  bf16x8 v[2][VLATE ? 1 : C];
   int row[2];
   uint32_t valid;
 };
 
+#ifndef KASCADE_DECODE_V_LATE
+#define KASCADE_DECODE_V_LATE 1
+#endif
+#ifndef KASCADE_GATHER_V_LATE
+#define KASCADE_GATHER_V_LATE 0
+#endif
+
 template <int D, bool GATHER, bool WITH_PV, bool LOGITS>
 __global__ __launch_bounds__(256) void decode_attn_bf16(DecodeArgs a) {
   constexpr int C = D / 32;  // contraction chunks of 32 along d
+  // The anchor's sweep requests V late (measured faster: its loads then
+  // trail the K stream); the short gathered lists request K and V together.
+  constexpr bool kVLate = GATHER ? KASCADE_GATHER_V_LATE != 0 : KASCADE_DECODE_V_LATE != 0;
+  using Stage = DecodeStage<C, kVLate>;
   const int lane = threadIdx.x & 63;
   const int split = blockIdx.x * kWavesPerBlock + wave_id();
   if (split >= a.splits) return;
@@ -104,7 +110,7 @@ __global__ __launch_bounds__(256) void decode_attn_bf16(DecodeArgs a) {
     int key = (GATHER && pos < end) ? list[pos] : -1;
     return (unsigned)key < (unsigned)a.n ? key : -1;
   };
-  auto load_stage = [&](DecodeStage<C>& st, int key_lane, int j0) __attribute__((always_inline)) {
+  auto load_stage = [&](Stage& st, int key_lane, int j0) __attribute__((always_inline)) {
     int row[2];
     if (GATHER) {
       st.valid = (uint32_t)__ballot(key_lane >= 0);
@@ -176,7 +182,7 @@ __global__ __launch_bounds__(256) void decode_attn_bf16(DecodeArgs a) {
     filled = 0;
   };
 
-  auto compute = [&](DecodeStage<C>& st, int j0) __attribute__((always_inline)) {
+  auto compute = [&](Stage& st, int j0) __attribute__((always_inline)) {
     float x[2][4];
     float cmax = kNegBig;
 #pragma unroll
@@ -245,7 +251,7 @@ __global__ __launch_bounds__(256) void decode_attn_bf16(DecodeArgs a) {
     }
   };
 
-  DecodeStage<C> s0, s1;
+  Stage s0, s1;
 #ifndef KASCADE_DECODE_PREFETCH
 #define KASCADE_DECODE_PREFETCH 1
 #endif
