@@ -155,7 +155,8 @@ __global__ __launch_bounds__(256) void decode_attn_bf16(DecodeArgs a) {
   int filled = 0;
   auto store_logits = [&](float* dst, const f32x4& v, uint32_t valid, int e0) __attribute__((always_inline)) {
     if ((valid >> (e0 + 3)) & 1u) {
-      *reinterpret_cast<f32x4*>(dst) = v;
+      // Streaming store: the scores are read once, by the selection kernel.
+      __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst));
     } else {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
