@@ -141,10 +141,10 @@ __global__ __launch_bounds__(256) void decode_attn_bf16(DecodeArgs a) {
 #pragma unroll
   for (int i = 0; i < D / 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Dense mode keeps the scores of up to `cap` chunks in LDS, each lane its
-  // own values, and writes them out together after the last of them: logit
-  // stores interleaved with the sweep's loads cost more than the same stores
-  // issued in one burst per wavefront.
+  // Dense mode keeps the scores of up to `cap` chunks in LDS and writes them
+  // out together after the last of them: logit stores interleaved with the
+  // sweep's loads cost more than the same stores issued in one burst per
+  // wavefront.
   constexpr bool kBuffered = LOGITS && !GATHER;
   // Per wavefront 16 KB (8 KB without P.V, 4 KB at d = 64), sized so that
   // the buffers never limit how many wavefronts a compute unit holds.
@@ -168,18 +168,26 @@ __global__ __launch_bounds__(256) void decode_attn_bf16(DecodeArgs a) {
   auto after_chunk = [&](int ci) __attribute__((always_inline)) {
     if (!kBuffered) return;
     if (++filled < cap && ci + 1 < nchunk) return;
-    if (n < G) {
-      for (int f = 0; f < filled; ++f) {
+    // Every lane writes: lane l takes the 16-byte piece l % 8 of (chunk, head)
+    // row l / 8 of the next eight, so each store instruction writes whole
+    // 128-byte lines of eight score rows. Lanes read scores that other lanes
+    // of the wavefront wrote to LDS; a wavefront's LDS operations complete in
+    // order.
+    __builtin_amdgcn_wave_barrier();
+    const int pairs = filled * G;  // (chunk, head) rows of 32 scores in the buffer
+    const int piece = lane & 7;
+    for (int p0 = 0; p0 < pairs; p0 += 8) {
+      const int P = p0 + (lane >> 3);
+      if (P < pairs) {
+        const int f = P / G, hn = P - f * G;
         const int j0 = begin + stride * (ci - filled + 1 + f);
         const int left = end - j0;
         const uint32_t valid = left >= 32 ? 0xffffffffu : ((1u << left) - 1u);
-        float* row = a.logits + (size_t)(b * a.hq + h0 + n) * a.logits_ld + j0 + 4 * qg;
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-          store_logits(row + 16 * t, *reinterpret_cast<const f32x4*>(lbuf + (f * G + n) * 32 + 16 * t + 4 * qg),
-                       valid, 16 * t + 4 * qg);
+        float* dst = a.logits + (size_t)(b * a.hq + h0 + hn) * a.logits_ld + j0 + 4 * piece;
+        store_logits(dst, *reinterpret_cast<const f32x4*>(lbuf + P * 32 + 4 * piece), valid, 4 * piece);
       }
     }
+    __builtin_amdgcn_wave_barrier();  // the next chunk's scores overwrite the buffer
     filled = 0;
   };
 
