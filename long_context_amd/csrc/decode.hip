@@ -172,8 +172,11 @@ __global__ __launch_bounds__(256) void decode_attn_bf16(DecodeArgs a) {
     // row l / 8 of the next eight, so each store instruction writes whole
     // 128-byte lines of eight score rows. Lanes read scores that other lanes
     // of the wavefront wrote to LDS; a wavefront's LDS operations complete in
-    // order.
+    // order, and the wavefront-scope fences keep the compiler from moving
+    // these reads above those writes.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const int pairs = filled * G;  // (chunk, head) rows of 32 scores in the buffer
     const int piece = lane & 7;
     for (int p0 = 0; p0 < pairs; p0 += 8) {
@@ -187,7 +190,10 @@ __global__ __launch_bounds__(256) void decode_attn_bf16(DecodeArgs a) {
         store_logits(dst, *reinterpret_cast<const f32x4*>(lbuf + P * 32 + 4 * piece), valid, 4 * piece);
       }
     }
-    __builtin_amdgcn_wave_barrier();  // the next chunk's scores overwrite the buffer
+    // The next chunk's scores overwrite the buffer.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     filled = 0;
   };
 
