@@ -35,6 +35,10 @@ CASES = {
     "bf16_k_eq_n": _small("bf16_k_eq_n", wid=905, n=640, k=640),
     "bf16_tiny": _small("bf16_tiny", wid=906, n=5, k=3, planted=1, batch=1),
     "bf16_n1": _small("bf16_n1", wid=907, n=1, k=1, planted=0, batch=1),
+    # Group sizes that do not divide the anchor's eight-row store groups, with
+    # a ragged last chunk: (chunk, head) score rows straddle store instructions.
+    "bf16_g3_ragged": _small("bf16_g3_ragged", wid=908, hq=6, hkv=2, n=2021, k=200),
+    "bf16_g6_d64": _small("bf16_g6_d64", wid=909, hq=12, hkv=2, d=64, n=1111, k=77),
 }
 
 
