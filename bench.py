@@ -211,13 +211,14 @@ def cpu_baseline(dec, threads, budget_s=20.0):
                        "reuse layer, timed and scaled to whole layers")}
 
 
-def profile_pass(kind, reps):
-    """Short runs for hardware-counter passes under rocprofv3.
+def profile_pass(kind, reps, workloads=("decode_llama8b_32k", "prefill_8k")):
+    """Short runs for hardware-counter and kernel-trace passes under rocprofv3.
 
     copy:    one plain elementwise kernel that reads 1 GiB and writes 1 GiB
              (negation of fp32), the known-size reference for FETCH_SIZE and
              WRITE_SIZE;
-    kernels: `reps` eager passes of the decode and prefill stacks.
+    kernels: `reps` eager passes of the layer stacks of `workloads` (by
+             default the benchmark's decode and prefill stacks).
     """
     dev = "cuda"
     if kind == "copy":
@@ -228,14 +229,16 @@ def profile_pass(kind, reps):
         torch.cuda.synchronize()
         print(json.dumps({"profile_pass": "copy", "read_bytes": 1 << 30, "write_bytes": 1 << 30}))
         return
-    dec = DecodeStack(synth.WORKLOADS["decode_llama8b_32k"], dev)
-    pre = PrefillStack(synth.WORKLOADS["prefill_8k"], dev)
+    stacks = []
+    for name in workloads:
+        w = synth.WORKLOADS[name]
+        stacks.append((DecodeStack if w.phase == "decode" else PrefillStack)(w, dev))
     torch.cuda.synchronize()
     for _ in range(reps):
-        dec.run()
-        pre.run()
+        for st in stacks:
+            st.run()
     torch.cuda.synchronize()
-    print(json.dumps({"profile_pass": "kernels", "reps": reps}), flush=True)
+    print(json.dumps({"profile_pass": "kernels", "reps": reps, "workloads": list(workloads)}), flush=True)
 
 
 # ---- accuracy against dense attention, swept over k -------------------------
@@ -385,6 +388,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
     ap.add_argument("--profile-pass", choices=("copy", "kernels"),
                     help="run a short pass for rocprofv3 counters instead of the benchmark")
+    ap.add_argument("--profile-workloads", default="decode_llama8b_32k,prefill_8k",
+                    help="comma-separated synthetic workloads for --profile-pass kernels")
     ap.add_argument("--sweep", action="store_true",
                     help="accuracy against dense attention over k = N/64 ... N/4 (one JSON line per k)")
     args = ap.parse_args()
@@ -396,7 +401,7 @@ def main():
         print("bench.py needs an MI355X GPU", file=sys.stderr)
         sys.exit(2)
     if args.profile_pass:
-        profile_pass(args.profile_pass, max(args.steps, 1))
+        profile_pass(args.profile_pass, max(args.steps, 1), tuple(args.profile_workloads.split(",")))
         return
     if args.sweep:
         for w in sweep_workloads():
