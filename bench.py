@@ -101,6 +101,11 @@ class DecodeStack:
             if marks is not None:
                 marks.append(("decode_reuse", _record()))
 
+    def run_dense(self):
+        """Dense attention in every layer (the anchor call without an index buffer)."""
+        for l, (q, k, v) in enumerate(self.layers):
+            K.anchor_decode(q, k, v, self.w.k, out=self.out[l], ws=self.ws_a, dense_only=True)
+
     def reuse_bytes(self):
         """Algorithmic bytes of one reuse layer: gathered K and V rows, idx, Q and O."""
         w = self.w
@@ -135,6 +140,11 @@ class PrefillStack:
             if marks is not None:
                 marks.append(("prefill_reuse", _record()))
 
+    def run_dense(self):
+        """Dense causal attention in every layer (no pooled scores, no selection)."""
+        for l, (q, k, v) in enumerate(self.layers):
+            K.anchor_prefill(q, k, v, self.w.k, self.w.tile, out=self.out[l], ws=self.ws_a, dense_only=True)
+
     def qk_flops(self):
         """Tile-granular causal QK^T flops of one pass over the sequence:
         every tile's G*T rows against its whole prefix of keys."""
@@ -165,50 +175,107 @@ def _record():
     return e
 
 
-def cpu_baseline(dec, threads, budget_s=20.0):
-    """The fp64 oracle on a bounded sample of the decode step, scaled to us/layer."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _timed(fn):
+    t0 = time.perf_counter()
+    r = fn()
+    return time.perf_counter() - t0, r
+
+
+def cpu_baseline(dec, pre, threads, prefill_tiles=96, prefill_rows=8192):
+    """The fp64 oracle, as it stands, timed on the host cores.
+
+    Each op is one oracle call over all its units, so the oracle's OpenMP loop
+    spreads them over `threads` threads (the count reported is what its
+    parallel region actually ran with).
+      * decode 32K: the whole anchor layer (pooled top-k over all B*Hkv units,
+        dense output and lse over all B*Hq rows) and one whole reuse layer over
+        the anchor's sets -- measured, not extrapolated; value = the mean of
+        one anchor and three reuse layers, us per layer, like the GPU figure;
+      * prefill 8K: the anchor's pooled top-k on `prefill_tiles` seeded
+        (KV head, tile) pairs, dense output and lse on `prefill_rows` seeded
+        rows, reuse on `prefill_rows` seeded rows; each scaled to the whole
+        layer by its per-unit cost (keys visited times heads, rows or d),
+        so the prefill figure is an extrapolation and is labelled so;
+      * a single-thread run of one decode unit gives the per-core rate."""
     import oracle
     orc = oracle.default()
+    used = orc.threads(threads)
     w = dec.w
     G = w.group
-    rng = np.random.default_rng(7)
-    units = [(int(b), int(kv)) for b, kv in zip(rng.integers(0, w.batch, 64), rng.integers(0, w.hkv, 64))]
-    q0, k0, v0 = dec.layers[0]
-    t_anchor, n_anchor = 0.0, 0
-    start = time.time()
-    for (b, kv) in units:
-        qs = synth.to_oracle(q0[b:b + 1, kv * G:(kv + 1) * G])
-        ks = synth.to_oracle(k0[b:b + 1, kv:kv + 1])
-        vs = synth.to_oracle(v0[b:b + 1, kv:kv + 1])
-        t0 = time.perf_counter()
-        orc.anchor_decode(qs, ks, w.k, threads=threads, want_pooled=False)
-        orc.dense(qs, ks, vs, causal=False, threads=threads)
-        t_anchor += time.perf_counter() - t0
-        n_anchor += 1
-        if time.time() - start > budget_s / 2:
-            break
-    anchor_layer = t_anchor / n_anchor * (w.batch * w.hkv)
-    # reuse: whole (b, kv) units of the first reuse layer with the saved sets
-    q1, k1, v1 = dec.layers[1]
-    idx = dec.idx.cpu().numpy()
-    t_reuse, n_reuse = 0.0, 0
-    start = time.time()
-    for (b, kv) in units:
-        qs = synth.to_oracle(q1[b:b + 1, kv * G:(kv + 1) * G])
-        ks = synth.to_oracle(k1[b:b + 1, kv:kv + 1])
-        vs = synth.to_oracle(v1[b:b + 1, kv:kv + 1])
-        t0 = time.perf_counter()
-        orc.reuse_decode(qs, ks, vs, idx[b:b + 1, kv:kv + 1], threads=threads)
-        t_reuse += time.perf_counter() - t0
-        n_reuse += 1
-        if time.time() - start > budget_s / 2:
-            break
-    reuse_layer = t_reuse / n_reuse * (w.batch * w.hkv)
-    us_per_layer = (anchor_layer + (w.layers - 1) * reuse_layer) / w.layers * 1e6
-    return {"value": us_per_layer, "unit": "us/layer", "cores": threads, "kind": "oracle",
-            "sample": (f"decode 32K: {n_anchor} of {w.batch * w.hkv} (batch, KV head) units of the "
-                       f"anchor layer (scores, pooled top-k, dense output) and {n_reuse} units of one "
-                       "reuse layer, timed and scaled to whole layers")}
+    q0, k0, v0 = (synth.to_oracle(t) for t in dec.layers[0])
+    t_sel, (io, _) = _timed(lambda: orc.anchor_decode(q0, k0, w.k, threads=threads, want_pooled=False))
+    t_dense, _ = _timed(lambda: orc.dense(q0, k0, v0, causal=False, threads=threads))
+    t_one, _ = _timed(lambda: orc.anchor_decode(q0[:1, :G], k0[:1, :1], w.k, threads=1, want_pooled=False))
+    t_one_d, _ = _timed(lambda: orc.dense(q0[:1, :G], k0[:1, :1], v0[:1, :1], causal=False, threads=1))
+    del k0, v0
+    q1, k1, v1 = (synth.to_oracle(t) for t in dec.layers[1])
+    idx = io.reshape(w.batch, w.hkv, 1, w.k)
+    t_reuse, _ = _timed(lambda: orc.reuse_decode(q1, k1, v1, idx, threads=threads))
+    del q1, k1, v1
+    anchor_s = t_sel + t_dense
+    dec_us = (anchor_s + (w.layers - 1) * t_reuse) / w.layers * 1e6
+
+    # prefill: sampled units, scaled to the layer by cost
+    wp = pre.w
+    T, tiles = wp.tile, wp.tiles
+    P0, K0, V0 = (synth.to_oracle(t) for t in pre.layers[0])
+    rng = np.random.default_rng(11)
+    prefix = np.minimum((np.arange(tiles) + 1) * T, wp.n)
+    rows_t = prefix - np.arange(tiles) * T
+    pairs = np.array([(0, i % wp.hkv, t) for i, t in enumerate(rng.choice(tiles, prefill_tiles))], np.int32)
+    t_pool, (ip, _) = _timed(lambda: orc.anchor_prefill(P0, K0, wp.k, T, units=pairs, threads=threads,
+                                                        want_pooled=False))
+    # pooled work of a tile ~ G * rows * prefix; the layer holds every (KV head, tile)
+    cost_tile = G * rows_t * prefix
+    pool_layer = t_pool * (wp.hkv * cost_tile.sum()) / cost_tile[pairs[:, 2]].sum()
+    flat = rng.choice(wp.hq * wp.n, prefill_rows, replace=False)
+    rows = np.stack([np.zeros(prefill_rows, np.int64), flat // wp.n, flat % wp.n], 1).astype(np.int32)
+    t_pd, _ = _timed(lambda: orc.dense(P0, K0, V0, causal=True, units=rows, threads=threads))
+    # dense work of row i ~ i + 1 keys
+    dense_layer = t_pd * (wp.hq * (wp.n * (wp.n + 1) / 2)) / (rows[:, 2] + 1).sum()
+    del P0, K0, V0
+    P1, K1, V1 = (synth.to_oracle(t) for t in pre.layers[1])
+    idxp = pre.idx.cpu().numpy()
+    t_pr, _ = _timed(lambda: orc.reuse_prefill(P1, K1, V1, idxp, T, units=rows, threads=threads))
+    # reuse work of row i ~ keys of its tile's set at or below i
+    kept = (idxp[0][:, :, None, :] >= 0) & (idxp[0][:, :, None, :] <= np.arange(T)[None, None, :, None]
+                                             + (np.arange(tiles) * T)[None, :, None, None])
+    per_row = kept.sum(-1).reshape(wp.hkv, tiles * T)[:, :wp.n]          # [Hkv, N]
+    row_cost = np.repeat(per_row, G, axis=0)                             # [Hq, N]
+    reuse_layer = t_pr * row_cost.sum() / max(1, row_cost[rows[:, 1], rows[:, 2]].sum())
+    del P1, K1, V1
+    pre_anchor_s = pool_layer + dense_layer
+    pre_tps = wp.batch * wp.n * wp.layers / (pre_anchor_s + (wp.layers - 1) * reuse_layer)
+    return {
+        "value": round(dec_us, 1), "unit": "us/layer", "cores": used, "kind": "oracle",
+        "sample": (f"decode 32K: whole layers -- anchor top-k over all {w.batch * w.hkv} (batch, KV head) "
+                   f"units and dense output/lse over all {w.batch * w.hq} rows, one reuse layer over all "
+                   f"rows -- mean of 1 anchor + {w.layers - 1} reuse layers; prefill 8K: {prefill_tiles} "
+                   f"(KV head, tile) anchor sets and {prefill_rows} rows each of dense and reuse attention, "
+                   "scaled to whole layers by per-unit cost (extrapolated)"),
+        "cpu_model": _cpu_model(),
+        "threads_requested": threads,
+        "decode_anchor_layer_s": round(anchor_s, 3),
+        "decode_reuse_layer_s": round(t_reuse, 4),
+        "decode_per_core_us_per_unit": round((t_one + t_one_d) * 1e6, 1),
+        "decode_per_core_note": ("one (batch, KV head) unit of the anchor layer (top-k of its 4 heads plus their "
+                                 "dense output) on one thread"),
+        "prefill_tokens_per_s": round(pre_tps, 2),
+        "prefill_tokens_per_s_kind": "extrapolated from the sampled units",
+        "prefill_anchor_layer_s": round(pre_anchor_s, 2),
+        "prefill_reuse_layer_s": round(reuse_layer, 2),
+    }
 
 
 def profile_pass(kind, reps, workloads=("decode_llama8b_32k", "prefill_8k")):
@@ -385,7 +452,6 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
     ap.add_argument("--profile-pass", choices=("copy", "kernels"),
                     help="run a short pass for rocprofv3 counters instead of the benchmark")
     ap.add_argument("--profile-workloads", default="decode_llama8b_32k,prefill_8k",
@@ -420,38 +486,48 @@ def main():
 
     for _ in range(args.warmup):
         step()
+        dec.run_dense()
+        pre.run_dense()
     torch.cuda.synchronize()
 
     # The step as two HIP graphs (decode stack, prefill stack): replays carry
-    # no host launch cost between the short kernels of a layer.
-    graphs = {}
+    # no host launch cost between the short kernels of a layer. The dense
+    # baseline (every layer plain dense attention, same tensors) is captured
+    # and timed the same way.
+    graphs, dense_graphs = {}, {}
     for name, stack in (("decode", dec), ("prefill", pre)):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            stack.run()
-        graphs[name] = g
+        for table, fn in ((graphs, stack.run), (dense_graphs, stack.run_dense)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn()
+            table[name] = g
     for _ in range(args.warmup):
-        for g in graphs.values():
+        for g in list(graphs.values()) + list(dense_graphs.values()):
             g.replay()
     torch.cuda.synchronize()
-    start_g, stop_g = _event(), _event()
-    gt = {n: 0.0 for n in graphs}
-    start_g.record()
+    # K steps bracketed by events, with an event after every step for the spread
+    start_g = _record()
+    step_ev = []
     for _ in range(args.steps):
         for g in graphs.values():
             g.replay()
-    stop_g.record()
+        step_ev.append(_record())
     torch.cuda.synchronize()
-    total_ms = start_g.elapsed_time(stop_g)
-    # per-stack time from a second pass that times each graph on its own
-    for n, g in graphs.items():
-        a, b = _event(), _event()
-        a.record()
+    total_ms = start_g.elapsed_time(step_ev[-1])
+    per_step = np.array([(start_g if i == 0 else step_ev[i - 1]).elapsed_time(e) for i, e in enumerate(step_ev)])
+
+    def time_graph(g):
+        """Per-replay times (ms) of one graph over args.steps replays."""
+        evs = [_record()]
         for _ in range(args.steps):
             g.replay()
-        b.record()
+            evs.append(_record())
         torch.cuda.synchronize()
-        gt[n] = a.elapsed_time(b) / args.steps
+        return np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
+
+    stack_ms = {n: time_graph(g) for n, g in graphs.items()}
+    dense_ms = {n: time_graph(g) for n, g in dense_graphs.items()}
+    gt = {n: float(v.mean()) for n, v in stack_ms.items()}
 
     # eager pass: per-call marks on the current stream and per-kernel events
     # inside the library
@@ -489,15 +565,14 @@ def main():
     dense_tflops = 2 * pre.qk_flops() / (kern["prefill_dense"] * 1e-3) / 1e12
     gather_tflops = pre.reuse_flops() / (kern["prefill_gather"] * 1e-3) / 1e12
 
-    # dense attention per layer: the anchor's dense pass with output (decode:
-    # the cache stream, which also writes the scaled logits, plus the split
-    # merge; prefill: causal flash attention with output and lse)
-    dense_dec_ms = kern["decode_attn_dense"] + kern["decode_combine"]
-    dense_pre_ms = kern["prefill_dense"]
+    # dense attention per layer: the graph of dense-only calls (no scores kept,
+    # no selection) over the same four layers, per layer
+    dense_dec_ms = float(dense_ms["decode"].mean()) / wd.layers
+    dense_pre_ms = float(dense_ms["prefill"].mean()) / wp.layers
 
     # dominant kernel: the largest share of the step
-    per_step = {n: kernels[n][0] / args.steps for n in kernels}
-    dominant = max(per_step, key=per_step.get)
+    share = {n: kernels[n][0] / args.steps for n in kernels}
+    dominant = max(share, key=share.get)
     rooflines = {
         "decode_attn_dense": ("hbm", anchor_gbs, PEAK_HBM_GBS, "GB/s", dec.anchor_bytes()),
         "decode_attn_gather": ("hbm", reuse_gbs, PEAK_HBM_GBS, "GB/s", dec.reuse_bytes()),
@@ -509,6 +584,10 @@ def main():
     roofline = {"kernel": dominant, "bound": bound, "achieved": round(achieved, 2), "peak": peak,
                 "unit": unit, "frac": round(achieved / peak, 4), "traffic": stored_traffic(dominant),
                 "work_per_launch": work, "avg_launch_ms": round(kern[dominant], 5)}
+
+    def spread(v, scale=1.0, nd=2):
+        return {"mean": round(float(v.mean()) * scale, nd), "median": round(float(np.median(v)) * scale, nd),
+                "min": round(float(v.min()) * scale, nd), "max": round(float(v.max()) * scale, nd)}
 
     result = {
         "metric": METRIC,
@@ -532,8 +611,9 @@ def main():
         "roofline": roofline,
         "metrics": {
             "decode_us_per_layer": round(t_dec_layer_ms * 1e3, 3),
-            "decode_stack_us_graph": round(gt["decode"] * 1e3, 2),
-            "prefill_stack_us_graph": round(gt["prefill"] * 1e3, 2),
+            "step_ms": spread(per_step, nd=4),
+            "decode_stack_us_graph": spread(stack_ms["decode"], 1e3),
+            "prefill_stack_us_graph": spread(stack_ms["prefill"], 1e3),
             "eager_ms_per_step": round(eager_ms_per_step, 4),
             "decode_anchor_us": round(avg["decode_anchor"] * 1e3, 2),
             "decode_reuse_us": round(avg["decode_reuse"] * 1e3, 2),
@@ -541,11 +621,14 @@ def main():
             "decode_reuse_hbm_gbs_call": round(reuse_call_gbs, 1),
             "decode_anchor_hbm_gbs_kernel": round(anchor_gbs, 1),
             "prefill_tokens_per_s": round(prefill_tps, 1),
-            # context: dense attention (the anchor's dense pass with output)
-            # per layer against the Kascade stack's mean layer
+            # context: dense attention per layer (dense-only calls, no scores
+            # kept, no selection, timed as a graph over the same four layers)
+            # against the Kascade stack's mean layer
             "dense_decode_layer_us": round(dense_dec_ms * 1e3, 2),
+            "dense_decode_stack_us_graph": spread(dense_ms["decode"], 1e3),
             "decode_speedup_vs_dense": round(dense_dec_ms / t_dec_layer_ms, 3),
             "dense_prefill_layer_us": round(dense_pre_ms * 1e3, 2),
+            "dense_prefill_stack_us_graph": spread(dense_ms["prefill"], 1e3),
             "prefill_speedup_vs_dense": round(dense_pre_ms / (t_pre_stack_ms / wp.layers), 3),
             "speedup_vs_dense_by_layers": {
                 str(L): {"decode": round(L * dense_dec_ms / (avg["decode_anchor"] + (L - 1) * avg["decode_reuse"]), 3),
@@ -564,7 +647,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
-        result["cpu_baseline"] = cpu_baseline(dec, threads, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(dec, pre, threads)
     print(json.dumps(result), flush=True)
 
 

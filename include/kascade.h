@@ -46,7 +46,12 @@
  *
  * Ownership and execution: every pointer is a device pointer owned by the
  * caller. The library allocates nothing; scratch memory is the caller's
- * workspace, sized by kascade_workspace_bytes(). Calls enqueue kernels on the
+ * workspace, sized by kascade_workspace_bytes(). A decode workspace (either
+ * decode op) begins with arrival counters that must be zero before its first
+ * use: zero-fill it once when it is allocated. Decode calls leave the counters
+ * zero again, so the same workspace serves any sequence of decode calls
+ * (including replays of a captured graph); do not hand a decode workspace to
+ * a prefill call in between. Calls enqueue kernels on the
  * given HIP stream (a hipStream_t passed as void*, NULL = the null stream) and
  * return without synchronising. Outputs are valid once the stream reaches
  * them. The idx buffer written by an anchor call is read by later reuse calls;
@@ -113,37 +118,60 @@ typedef struct {
 int kascade_validate(const kascade_problem* p, int op);
 
 /* Bytes of device workspace the op needs for this problem (0 for an invalid
- * problem). The workspace must be 256-byte aligned. */
+ * problem). The workspace must be 256-byte aligned; decode workspaces must be
+ * zero-filled once when allocated (see above). */
 size_t kascade_workspace_bytes(const kascade_problem* p, int op);
 
 /* Anchor layer, one decode query per (batch, query head).
+ * Defined by: the anchor layer's dense attention pass, post-softmax scores
+ * reduced to exact top-k indices per head (Kascade abstract, opentrain.ai
+ * page, "Abstract"; euno.news summary, "Methodology" steps 2 and 5).
  * Computes dense scores of q against all N keys, the per-KV-head pooled
  * post-softmax score, and its exact top-k into idx [B, S, 1, k].
  * out (nullable): dense attention output [B, Hq, 1, d] (reads V; v may be
- * NULL when out is NULL). lse (nullable): [B, Hq, 1]. */
+ * NULL when out is NULL). lse (nullable): [B, Hq, 1].
+ * idx (nullable): when NULL the call is plain dense attention -- no scores
+ * are kept and nothing is selected -- for layers that attend densely without
+ * refreshing an index set; out or lse must then be given.
+ * Workspace: kascade_workspace_bytes(p, KASCADE_OP_ANCHOR_DECODE). */
 int kascade_anchor_decode(const kascade_problem* p, const void* q, const void* k,
                           const void* v, void* out, int32_t* idx, float* lse,
                           void* workspace, size_t workspace_bytes, void* stream);
 
-/* Reuse layer, decode. For each (b, h): softmax attention of q over the keys
- * idx[b, h/G, 0, :] (idx[b, 0, 0, :] with a shared set) with this layer's K
- * and V, written to out [B, Hq, 1, d].
+/* Reuse layer, decode. Defined by: a reuse layer attends only to the keys
+ * saved by the preceding anchor, softmax restricted to that set, with its own
+ * Q, K and V (euno.news summary, "Methodology" step 3; Kascade abstract,
+ * opentrain.ai page, "Abstract").
+ * For each (b, h): softmax attention of q over the keys idx[b, h/G, 0, :]
+ * (idx[b, 0, 0, :] with a shared set) with this layer's K and V, written to
+ * out [B, Hq, 1, d].
  * Entries -1 (and any entry outside [0, N)) are skipped; a row whose list has
  * no usable entry gets zeros. */
 int kascade_reuse_decode(const kascade_problem* p, const void* q, const void* k,
                          const void* v, const int32_t* idx, void* out,
                          void* workspace, size_t workspace_bytes, void* stream);
 
-/* Anchor layer, causal prefill. For each (b, KV head, query tile t): the mean
+/* Anchor layer, causal prefill. Defined by: exact top-k selection in the
+ * anchor layer, done per query tile in prefill (Kascade abstract, opentrain.ai
+ * page, "Abstract": tile-level operations; euno.news summary, "Methodology"
+ * steps 2, 5 and 6).
+ * For each (b, KV head, query tile t): the mean
  * over the tile's rows and the group's heads of the causal post-softmax
  * probabilities (all heads' with a shared set), and its exact top-k_t among
  * keys < prefix_t into idx [B, S, ceil(N/T), k]. out (nullable): dense causal attention output
- * [B, Hq, N, d]. lse (nullable): [B, Hq, N]. */
+ * [B, Hq, N, d]. lse (nullable): [B, Hq, N].
+ * idx (nullable): when NULL the call is plain dense causal attention (no
+ * pooled scores, no selection); out or lse must then be given.
+ * Workspace: kascade_workspace_bytes(p, KASCADE_OP_ANCHOR_PREFILL). */
 int kascade_anchor_prefill(const kascade_problem* p, const void* q, const void* k,
                            const void* v, void* out, int32_t* idx, float* lse,
                            void* workspace, size_t workspace_bytes, void* stream);
 
-/* Reuse layer, causal prefill. Row i of tile t attends to the keys
+/* Reuse layer, causal prefill. Defined by: each query tile of a reuse layer
+ * attends only to its tile's saved index set, causally, with the layer's own
+ * Q, K and V (euno.news summary, "Methodology" steps 3 and 6; Kascade
+ * abstract, opentrain.ai page, "Abstract").
+ * Row i of tile t attends to the keys
  * j in idx[b, h/G, t, 0:k_t] (set 0 when shared) with 0 <= j <= i (entries -1, or outside the
  * sequence, are skipped); a row with no such key gets zeros. Output
  * out [B, Hq, N, d]. Slots at or past k_t = min(k, prefix_t) are not read. */

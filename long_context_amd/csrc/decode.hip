@@ -53,16 +53,117 @@ struct DecodeStage {
 #define KASCADE_GATHER_V_LATE 0
 #endif
 
-template <int D, bool GATHER, bool WITH_PV, bool LOGITS>
-__global__ __launch_bounds__(256) void decode_attn_bf16(DecodeArgs a) {
+// Fused split merge of the reuse gather (Kascade reuse layer: the softmax of
+// each query row restricted to the saved set, merged over the splits that
+// share that set). Every wavefront of the workgroup holds, per head column
+// n < G of the group, its running maximum m (log2 units), its sum l and its
+// unnormalised output acc (element r of acc[i] is d = 16i + 4qg + r).
+//   1. The wavefronts' (m, l, acc) go to LDS and the workgroup merges them
+//      (one output element per thread and step): M = max m_w,
+//      L = sum l_w 2^(m_w - M), O = sum acc_w 2^(m_w - M).
+//   2. One workgroup per (b, KV head): out = O / L (0 if L = 0).
+//      Otherwise (M, L, O) go to the partial arrays, and the workgroup takes a
+//      ticket on counters[unit]; the workgroup holding the last ticket
+//      (gridDim.x - 1) merges the workgroups' partials the same way, writes
+//      out and sets the counter back to 0 for the next call.
+// Publishing the partials: they are written and read with device-coherent
+// (agent-scope) accesses, which bypass the per-XCD L2 caches, and every
+// thread waits for its partial stores to complete before the workgroup's
+// ticket is taken. A device-scope fence would do the same by writing back
+// and invalidating its XCD's whole L2, once per workgroup: measured three
+// times slower than the gather itself.
+// Device-coherent (agent-scope) float store and load.
+__device__ __forceinline__ void coherent_store(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float coherent_load(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int D, int WPB>
+__device__ __forceinline__ void merge_group(const DecodeArgs& a, int b, int kvh, float m, float l,
+                                            const f32x4 (&acc)[D / 16]) {
+  extern __shared__ __attribute__((aligned(16))) float merge_lds[];
+  __shared__ int is_last;
+  const int G = a.group;
+  const int lane = threadIdx.x & 63, n = lane & 15, qg = lane >> 4;
+  const int w = wave_id();
+  float* red_ml = merge_lds;                      // [WPB][G][2]
+  float* red_o = merge_lds + WPB * G * 2;         // [WPB][G][D], 16-byte aligned (G*2*4*WPB % 16 == 0)
+  if (n < G) {
+    if (qg == 0) {
+      red_ml[(w * G + n) * 2] = m;
+      red_ml[(w * G + n) * 2 + 1] = l;
+    }
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i)
+      *reinterpret_cast<f32x4*>(&red_o[(w * G + n) * D + 16 * i + 4 * qg]) = acc[i];
+  }
+  __syncthreads();
+  const int unit = b * a.hkv + kvh;
+  const int wgs = gridDim.x, wg = blockIdx.x;
+  const int nout = G * D;
+  u16* out = static_cast<u16*>(a.out) + (size_t)(b * a.hq + kvh * G) * D;
+  for (int o = threadIdx.x; o < nout; o += 64 * WPB) {
+    const int g = o / D, c = o - g * D;
+    float M = kNegBig;
+#pragma unroll
+    for (int v = 0; v < WPB; ++v) M = fmaxf(M, red_ml[(v * G + g) * 2]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int v = 0; v < WPB; ++v) {
+      const float wt = fast_exp2(red_ml[(v * G + g) * 2] - M);
+      L += red_ml[(v * G + g) * 2 + 1] * wt;
+      O += red_o[(v * G + g) * D + c] * wt;
+    }
+    if (wgs == 1) {
+      out[o] = float_to_bf16_bits(L > 0.f ? O / L : 0.f);
+    } else {
+      const size_t slot = ((size_t)unit * wgs + wg) * G + g;
+      coherent_store(&a.part_o[slot * D + c], O);
+      if (c == 0) {
+        coherent_store(&a.part_ml[2 * slot], M);
+        coherent_store(&a.part_ml[2 * slot + 1], L);
+      }
+    }
+  }
+  if (wgs == 1) return;
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's partial stores are complete
+  __syncthreads();
+  if (threadIdx.x == 0)
+    is_last = __hip_atomic_fetch_add(&a.counters[unit], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == wgs - 1;
+  __syncthreads();
+  if (!is_last) return;
+  const float* pml = a.part_ml + (size_t)unit * wgs * G * 2;
+  const float* po = a.part_o + (size_t)unit * wgs * G * D;
+  for (int o = threadIdx.x; o < nout; o += 64 * WPB) {
+    const int g = o / D, c = o - g * D;
+    float M = kNegBig;
+    for (int v = 0; v < wgs; ++v) M = fmaxf(M, coherent_load(&pml[(v * G + g) * 2]));
+    float L = 0.f, O = 0.f;
+    for (int v = 0; v < wgs; ++v) {
+      const float wt = fast_exp2(coherent_load(&pml[(v * G + g) * 2]) - M);
+      L += coherent_load(&pml[(v * G + g) * 2 + 1]) * wt;
+      O += coherent_load(&po[(size_t)(v * G + g) * D + c]) * wt;
+    }
+    out[o] = float_to_bf16_bits(L > 0.f ? O / L : 0.f);
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(&a.counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// MERGE (gather only): WPB wavefronts per workgroup, splits = gridDim.x * WPB;
+// the split merge runs at the end of the kernel instead of in decode_combine.
+template <int D, bool GATHER, bool WITH_PV, bool LOGITS, int WPB = kWavesPerBlock, bool MERGE = false>
+__global__ __launch_bounds__(64 * WPB) void decode_attn_bf16(DecodeArgs a) {
+  static_assert(!MERGE || (GATHER && WITH_PV && !LOGITS), "the fused merge is for the reuse gather");
   constexpr int C = D / 32;  // contraction chunks of 32 along d
   // The anchor's sweep requests V late (measured faster: its loads then
   // trail the K stream); the short gathered lists request K and V together.
   constexpr bool kVLate = GATHER ? KASCADE_GATHER_V_LATE != 0 : KASCADE_DECODE_V_LATE != 0;
   using Stage = DecodeStage<C, kVLate>;
   const int lane = threadIdx.x & 63;
-  const int split = blockIdx.x * kWavesPerBlock + wave_id();
-  if (split >= a.splits) return;
+  const int split = blockIdx.x * WPB + wave_id();
+  if (!MERGE && split >= a.splits) return;  // merged launches have no partial workgroups
   const int kvh = blockIdx.y, b = blockIdx.z;
   const int n = lane & 15;   // head column (B operand / C column) and A-operand row
   const int qg = lane >> 4;  // lane group: contraction slots 8*qg..8*qg+7
@@ -98,7 +199,7 @@ __global__ __launch_bounds__(256) void decode_attn_bf16(DecodeArgs a) {
   // front to back in step rather than each streaming a region of its own.
   constexpr bool kInterleave = !GATHER && KASCADE_DENSE_INTERLEAVE;
   const int begin = kInterleave ? 32 * split : split * a.keys_per_split;
-  const int end = kInterleave ? a.list_len : min(begin + a.keys_per_split, a.list_len);
+  const int end = kInterleave ? a.list_len : max(begin, min(begin + a.keys_per_split, a.list_len));
   const int stride = kInterleave ? 32 * a.splits : 32;  // keys between a split's chunks
   const int nchunk = kInterleave ? (begin < end ? (end - begin + stride - 1) / stride : 0)
                                  : (end - begin + 31) / 32;
@@ -307,6 +408,10 @@ __global__ __launch_bounds__(256) void decode_attn_bf16(DecodeArgs a) {
   }
 
   l = group4_sum(l);
+  if constexpr (MERGE) {
+    merge_group<D, WPB>(a, b, kvh, m, l, acc);
+    return;
+  }
   if (n < G) {
     const size_t slot = (size_t)(b * a.hq + h0 + n) * a.splits + split;
     if (qg == 0) {
@@ -522,6 +627,19 @@ hipError_t launch_decode_attn(const DecodeArgs& a, bool bf16, bool gather, bool 
   if (a.d == 64) return launch_attn_d<64>(a, bf16, gather, with_pv, s);
   if (a.d == 128) return launch_attn_d<128>(a, bf16, gather, with_pv, s);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_gather_merged(const DecodeArgs& a, hipStream_t s) {
+  if (a.splits % kGatherWaves != 0 || a.group > 16) return hipErrorInvalidValue;
+  const dim3 grid(a.splits / kGatherWaves, a.hkv, a.batch), block(64 * kGatherWaves);
+  const size_t lds = gather_merge_lds_bytes(a.group, a.d);
+  if (a.d == 128)
+    hipLaunchKernelGGL((decode_attn_bf16<128, true, true, false, kGatherWaves, true>), grid, block, lds, s, a);
+  else if (a.d == 64)
+    hipLaunchKernelGGL((decode_attn_bf16<64, true, true, false, kGatherWaves, true>), grid, block, lds, s, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 hipError_t launch_decode_combine(const float* part_ml, const float* part_o, int rows, int splits,

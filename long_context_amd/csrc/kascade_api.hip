@@ -84,19 +84,41 @@ DecodeSplit decode_split(const kascade_problem* p, int len, bool dense) {
 
 struct DecodeWorkspace {
   DecodeSplit split;
-  size_t part_ml, part_o, logits, lse2, pooled, cand_val, cand_idx, total;  // byte offsets
+  bool merged;  // bf16 reuse: split merge fused into the gather (workgroup partials)
+  size_t counters, part_ml, part_o, logits, lse2, pooled, cand_val, cand_idx, total;  // byte offsets
 };
+
+// bf16 reuse decode fuses the split merge into the gather: the splits come in
+// workgroups of kGatherWaves wavefronts, and the partials are per workgroup.
+DecodeSplit gather_split(const kascade_problem* p) {
+  DecodeSplit s = decode_split(p, p->top_k, false);
+  s.splits = (s.splits + kGatherWaves - 1) / kGatherWaves * kGatherWaves;
+  return s;
+}
+
+// Every decode workspace begins with the reuse gather's arrival counters
+// (B*Hkv int32). They must be zero before a reuse call; the reuse call leaves
+// them zero, and the anchor call never writes them, so one zero-filled decode
+// workspace serves any sequence of decode calls.
+size_t counters_bytes(const kascade_problem* p) {
+  return align_up((size_t)p->batch * p->num_kv_heads * sizeof(int32_t));
+}
 
 DecodeWorkspace decode_workspace(const kascade_problem* p, int op) {
   DecodeWorkspace w{};
   const bool anchor = op == KASCADE_OP_ANCHOR_DECODE;
-  w.split = decode_split(p, anchor ? p->kv_len : p->top_k, anchor);
+  w.merged = !anchor && p->dtype == KASCADE_BF16;
+  w.split = w.merged ? gather_split(p) : decode_split(p, anchor ? p->kv_len : p->top_k, anchor);
   const size_t rows = (size_t)p->batch * p->num_q_heads;
+  // partial slots: per (row, split), or per (row, workgroup) when merged
+  const size_t slots = rows * (w.merged ? w.split.splits / kGatherWaves : w.split.splits);
   size_t off = 0;
+  w.counters = off;
+  off += counters_bytes(p);
   w.part_ml = off;
-  off += align_up(rows * w.split.splits * 2 * sizeof(float));
+  off += align_up(slots * 2 * sizeof(float));
   w.part_o = off;
-  off += align_up(rows * w.split.splits * p->head_dim * sizeof(float));
+  off += align_up(slots * p->head_dim * sizeof(float));
   if (anchor) {
     w.logits = off;
     off += align_up(rows * decode_logits_ld(p->kv_len) * sizeof(float));
@@ -236,6 +258,7 @@ DecodeArgs decode_args(const kascade_problem* p, const void* q, const void* k, c
   a.scale_log2 = scale_log2(p);
   a.part_ml = reinterpret_cast<float*>(ws + w.part_ml);
   a.part_o = reinterpret_cast<float*>(ws + w.part_o);
+  a.counters = reinterpret_cast<int*>(ws + w.counters);
   a.logits = nullptr;
   a.logits_ld = decode_logits_ld(p->kv_len);
   return a;
@@ -287,9 +310,10 @@ int kascade_anchor_decode(const kascade_problem* p, const void* q, const void* k
                           size_t workspace_bytes, void* stream) {
   int rc = validate(p, KASCADE_OP_ANCHOR_DECODE);
   if (rc) return rc;
-  if (!q || !k || !idx || (out && !v)) return KASCADE_ERR_INVALID;
+  // idx NULL: dense attention only (out and/or lse), no scores kept, no selection.
+  if (!q || !k || (out && !v) || (!idx && !out && !lse)) return KASCADE_ERR_INVALID;
   if (!aligned16(q) || !aligned16(k) || (v && !aligned16(v)) || (out && !aligned16(out)) ||
-      !aligned4(idx) || (lse && !aligned4(lse)))
+      (idx && !aligned4(idx)) || (lse && !aligned4(lse)))
     return KASCADE_ERR_INVALID;
   rc = check_workspace(p, KASCADE_OP_ANCHOR_DECODE, workspace, workspace_bytes);
   if (rc) return rc;
@@ -298,10 +322,16 @@ int kascade_anchor_decode(const kascade_problem* p, const void* q, const void* k
   char* ws = static_cast<char*>(workspace);
   DecodeArgs a = decode_args(p, q, k, v, nullptr, w, ws);
   a.list_len = p->kv_len;
+  const bool bf16 = p->dtype == KASCADE_BF16;
+  if (!idx) {
+    KASCADE_TRY("decode_attn_dense_only", launch_decode_attn(a, bf16, false, out != nullptr, s));
+    KASCADE_TRY("decode_combine", launch_decode_combine(a.part_ml, a.part_o, p->batch * a.hq, a.splits,
+                                                        a.d, bf16, out, lse, nullptr, s));
+    return KASCADE_OK;
+  }
   a.logits = reinterpret_cast<float*>(ws + w.logits);
   float* pooled = reinterpret_cast<float*>(ws + w.pooled);
   float* lse2 = reinterpret_cast<float*>(ws + w.lse2);
-  const bool bf16 = p->dtype == KASCADE_BF16;
   KASCADE_TRY("decode_attn_dense", launch_decode_attn(a, bf16, false, out != nullptr, s));
   KASCADE_TRY("decode_combine", launch_decode_combine(a.part_ml, a.part_o, p->batch * a.hq,
                                                       a.splits, a.d, bf16, out, lse, lse2, s));
@@ -334,10 +364,14 @@ int kascade_reuse_decode(const kascade_problem* p, const void* q, const void* k,
   const DecodeWorkspace w = decode_workspace(p, KASCADE_OP_REUSE_DECODE);
   DecodeArgs a = decode_args(p, q, k, v, idx, w, static_cast<char*>(workspace));
   a.list_len = p->top_k;
-  const bool bf16 = p->dtype == KASCADE_BF16;
-  KASCADE_TRY("decode_attn_gather", launch_decode_attn(a, bf16, true, true, s));
+  a.out = out;
+  if (w.merged) {
+    KASCADE_TRY("decode_attn_gather", launch_decode_gather_merged(a, s));
+    return KASCADE_OK;
+  }
+  KASCADE_TRY("decode_attn_gather", launch_decode_attn(a, false, true, true, s));
   KASCADE_TRY("decode_combine", launch_decode_combine(a.part_ml, a.part_o, p->batch * a.hq,
-                                                      a.splits, a.d, bf16, out, nullptr, nullptr, s));
+                                                      a.splits, a.d, false, out, nullptr, nullptr, s));
   return KASCADE_OK;
 }
 
@@ -346,9 +380,10 @@ int kascade_anchor_prefill(const kascade_problem* p, const void* q, const void* 
                            size_t workspace_bytes, void* stream) {
   int rc = validate(p, KASCADE_OP_ANCHOR_PREFILL);
   if (rc) return rc;
-  if (!q || !k || !idx || (out && !v)) return KASCADE_ERR_INVALID;
+  // idx NULL: dense causal attention only (out and/or lse), no pooled scores, no selection.
+  if (!q || !k || (out && !v) || (!idx && !out && !lse)) return KASCADE_ERR_INVALID;
   if (!aligned16(q) || !aligned16(k) || (v && !aligned16(v)) || (out && !aligned16(out)) ||
-      !aligned4(idx) || (lse && !aligned4(lse)))
+      (idx && !aligned4(idx)) || (lse && !aligned4(lse)))
     return KASCADE_ERR_INVALID;
   rc = check_workspace(p, KASCADE_OP_ANCHOR_PREFILL, workspace, workspace_bytes);
   if (rc) return rc;
@@ -359,16 +394,18 @@ int kascade_anchor_prefill(const kascade_problem* p, const void* q, const void* 
   PrefillArgs a = prefill_args(p, q, k, out ? v : k, nullptr, out);
   a.lse2 = reinterpret_cast<float*>(ws + w.lse2);
   a.pooled = reinterpret_cast<float*>(ws + w.pooled);
-  KASCADE_TRY("prefill_dense", launch_prefill_dense(a, s));
-  KASCADE_TRY("prefill_pool", launch_prefill_pool(a, s));
-  if (p->shared_index_set) {
-    float* shared = reinterpret_cast<float*>(ws + w.shared);
-    KASCADE_TRY("sum_sets", launch_sum_sets(a.pooled, p->batch, a.hkv,
-                                            prefill_ragged_len(a.n, a.tile), shared, s));
-    KASCADE_TRY("topk_prefill", launch_topk_prefill(shared, p->batch, 1, a.n, a.tile, p->top_k, idx, s));
-  } else {
-    KASCADE_TRY("topk_prefill", launch_topk_prefill(a.pooled, p->batch, a.hkv, a.n, a.tile, p->top_k,
-                                                    idx, s));
+  KASCADE_TRY(idx ? "prefill_dense" : "prefill_dense_only", launch_prefill_dense(a, s));
+  if (idx) {
+    KASCADE_TRY("prefill_pool", launch_prefill_pool(a, s));
+    if (p->shared_index_set) {
+      float* shared = reinterpret_cast<float*>(ws + w.shared);
+      KASCADE_TRY("sum_sets", launch_sum_sets(a.pooled, p->batch, a.hkv,
+                                              prefill_ragged_len(a.n, a.tile), shared, s));
+      KASCADE_TRY("topk_prefill", launch_topk_prefill(shared, p->batch, 1, a.n, a.tile, p->top_k, idx, s));
+    } else {
+      KASCADE_TRY("topk_prefill", launch_topk_prefill(a.pooled, p->batch, a.hkv, a.n, a.tile, p->top_k,
+                                                      idx, s));
+    }
   }
   if (lse)
     KASCADE_TRY("lse_convert", launch_lse2_to_lse(a.lse2, lse, (size_t)p->batch * a.hq * a.n, s));

@@ -25,7 +25,21 @@ struct DecodeArgs {
   float* part_o;         // [B*Hq*splits][d]: unnormalised partial output
   float* logits;         // dense mode, optional: [B, Hq, logits_ld] scaled logits, log2 units
   int logits_ld;         // row stride of logits: N rounded up to a multiple of 4
+  // Gather with the split merge fused in (bf16): the workgroups of a (b, KV
+  // head) each merge their wavefronts in LDS; with more than one workgroup per
+  // (b, KV head) they leave partials in part_ml / part_o, laid out
+  // [unit][workgroup][head of the group] (x2, xd), and the last to arrive on
+  // counters[unit] merges them into out and sets the counter back to 0.
+  int* counters;         // [B*Hkv] arrival counters, zero between calls
+  void* out;             // [B, Hq, 1, d] bf16
 };
+
+// Wavefronts per workgroup of the fused gather; splits are a multiple of it.
+constexpr int kGatherWaves = 8;
+__host__ __device__ inline size_t gather_merge_lds_bytes(int group, int d) {
+  return (size_t)kGatherWaves * group * (d + 2) * sizeof(float);
+}
+hipError_t launch_decode_gather_merged(const DecodeArgs& a, hipStream_t s);
 
 __host__ __device__ inline int decode_logits_ld(int n) { return (n + 3) & ~3; }
 

@@ -178,9 +178,11 @@ def _stream(stream):
 
 
 def workspace(prob, op, device):
-    """A workspace tensor of kascade_workspace_bytes() bytes (None if zero)."""
+    """A zero-filled workspace tensor of kascade_workspace_bytes() bytes (None
+    if zero). Decode workspaces must start zeroed (their arrival counters);
+    every call leaves them so."""
     n = library().workspace_bytes(prob, op)
-    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+    return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
 
 
 def _ws(ws):
@@ -188,14 +190,18 @@ def _ws(ws):
 
 
 def anchor_decode(q, k, v, top_k, out=None, lse=None, idx=None, ws=None, scale=0.0, stream=None,
-                  shared=False):
+                  shared=False, dense_only=False):
     """Anchor decode; returns idx [B,S,1,k] int32, S = Hkv or 1 with shared=True
-    (and fills out/lse if given)."""
+    (and fills out/lse if given). dense_only=True passes no index buffer: the
+    call is plain dense attention into out/lse and returns None."""
     lib = library()
     prob = problem(q, k, top_k, 1, scale, shared)
-    if idx is None:
-        idx = torch.empty(idx_shape(prob), dtype=torch.int32, device=q.device)
-    _check_idx(idx, prob, "anchor_decode")
+    if dense_only:
+        idx = None
+    else:
+        if idx is None:
+            idx = torch.empty(idx_shape(prob), dtype=torch.int32, device=q.device)
+        _check_idx(idx, prob, "anchor_decode")
     if ws is None:
         ws = workspace(prob, OP_ANCHOR_DECODE, q.device)
     wp, wb = _ws(ws)
@@ -220,13 +226,18 @@ def reuse_decode(q, k, v, idx, out=None, ws=None, scale=0.0, stream=None, shared
 
 
 def anchor_prefill(q, k, v, top_k, q_tile=128, out=None, lse=None, idx=None, ws=None, scale=0.0,
-                   stream=None, shared=False):
-    """Anchor causal prefill; returns idx [B,S,ceil(N/T),k] int32, S = Hkv or 1 with shared=True."""
+                   stream=None, shared=False, dense_only=False):
+    """Anchor causal prefill; returns idx [B,S,ceil(N/T),k] int32, S = Hkv or 1 with shared=True.
+    dense_only=True passes no index buffer: plain dense causal attention into
+    out/lse, returns None."""
     lib = library()
     prob = problem(q, k, top_k, q_tile, scale, shared)
-    if idx is None:
-        idx = torch.empty(idx_shape(prob), dtype=torch.int32, device=q.device)
-    _check_idx(idx, prob, "anchor_prefill")
+    if dense_only:
+        idx = None
+    else:
+        if idx is None:
+            idx = torch.empty(idx_shape(prob), dtype=torch.int32, device=q.device)
+        _check_idx(idx, prob, "anchor_prefill")
     if ws is None:
         ws = workspace(prob, OP_ANCHOR_PREFILL, q.device)
     wp, wb = _ws(ws)
@@ -281,7 +292,8 @@ def kascade_attention(qs, ks, vs, top_k, anchors, q_tile=128, outs=None, scale=0
     """Kascade attention over a stack of layers, one call per layer through the
     C ABI. qs, ks, vs: per-layer tensors, decode (Q [B,Hq,1,d]) or causal
     prefill (Q [B,Hq,N,d]), K/V [B,Hkv,N,d]. Layers before the first anchor
-    attend densely (the anchor call's dense output; its indices are not kept),
+    attend densely (the anchor call without an index buffer: dense output
+    only, no scores kept and no selection),
     an anchor layer outputs dense attention and saves its top-k indices, every
     other layer attends only to the saved indices of the nearest preceding
     anchor, with its own Q, K and V. shared=True runs the non-head-aware
@@ -299,18 +311,20 @@ def kascade_attention(qs, ks, vs, top_k, anchors, q_tile=128, outs=None, scale=0
     for l, (role, src) in enumerate(roles):
         q, k, v = qs[l], ks[l], vs[l]
         if role in ("dense", "anchor"):
-            kk = min(top_k, n) if (decode or role == "dense") else top_k
+            # Dense layers pass no index buffer: no scores are kept, nothing is selected.
+            kk = min(top_k, n) if decode else top_k
+            dense_only = role == "dense"
             if decode:
                 if ws_anchor is None:
                     ws_anchor = workspace(problem(q, k, kk, 1, scale, shared), OP_ANCHOR_DECODE, q.device)
                 idx = anchor_decode(q, k, v, kk, out=outs[l], ws=ws_anchor, scale=scale, stream=stream,
-                                    shared=shared)
+                                    shared=shared, dense_only=dense_only)
             else:
                 if ws_anchor is None:
                     ws_anchor = workspace(problem(q, k, kk, q_tile, scale, shared), OP_ANCHOR_PREFILL,
                                           q.device)
                 idx = anchor_prefill(q, k, v, kk, q_tile, out=outs[l], ws=ws_anchor, scale=scale,
-                                     stream=stream, shared=shared)
+                                     stream=stream, shared=shared, dense_only=dense_only)
             if role == "anchor":
                 saved[l] = idx
         elif decode:

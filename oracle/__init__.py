@@ -81,8 +81,9 @@ class Oracle:
         lib.oracle_reuse_decode.argtypes = [P, vp, vp, vp, _c_int_p, _c_int_p, ctypes.c_int, _c_dbl_p, ctypes.c_int]
         lib.oracle_reuse_prefill.argtypes = [P, vp, vp, vp, _c_int_p, _c_int_p, ctypes.c_int, _c_dbl_p, ctypes.c_int]
         lib.oracle_dense.argtypes = [P, vp, vp, vp, ctypes.c_int, _c_int_p, ctypes.c_int, _c_dbl_p, _c_dbl_p, ctypes.c_int]
+        lib.oracle_threads.argtypes = [ctypes.c_int]
         for f in (lib.oracle_anchor_decode, lib.oracle_anchor_prefill, lib.oracle_reuse_decode,
-                  lib.oracle_reuse_prefill, lib.oracle_dense):
+                  lib.oracle_reuse_prefill, lib.oracle_dense, lib.oracle_threads):
             f.restype = ctypes.c_int
         self.lib = lib
 
@@ -98,6 +99,10 @@ class Oracle:
     def _check(self, rc, name):
         if rc != 0:
             raise ValueError(f"{name} failed with status {rc}")
+
+    def threads(self, nthreads=0):
+        """Threads the oracle's parallel loops run with for `nthreads` (0 = default)."""
+        return int(self.lib.oracle_threads(int(nthreads)))
 
     # -- anchor -------------------------------------------------------------
     def anchor_decode(self, q, k, top_k, units=None, scale=None, threads=0, want_pooled=True, shared=False):

@@ -395,3 +395,16 @@ int oracle_dense(const oracle_problem* p, const void* q, const void* k, const vo
   }
   return status;
 }
+
+/* ---- thread count --------------------------------------------------------- */
+
+int oracle_threads(int nthreads) {
+  int used = 0;
+  set_threads(nthreads);
+#pragma omp parallel
+  {
+#pragma omp single
+    used = omp_get_num_threads();
+  }
+  return used;
+}

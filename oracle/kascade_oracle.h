@@ -104,6 +104,10 @@ int oracle_dense(const oracle_problem* p, const void* q, const void* k, const vo
                  int causal, const int32_t* units, int nunits,
                  double* out, double* lse, int nthreads);
 
+/* Threads an OpenMP parallel region of the oracle runs with when asked for
+ * nthreads (0 = the OpenMP default). No arithmetic; for reporting only. */
+int oracle_threads(int nthreads);
+
 #ifdef __cplusplus
 }
 #endif

@@ -141,7 +141,11 @@ def test_entry_points_reject_before_launch(L):
     assert L.reuse_decode_raw(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 16, ws_rd, None) == K.ERR_WORKSPACE
     pp = _prefill()
     ws_ap = L.workspace_bytes(pp, K.OP_ANCHOR_PREFILL)
-    assert L.anchor_prefill_raw(pp, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, ws_ap, None) == K.ERR_INVALID
+    # without an index buffer the anchor call is dense attention only: it needs out or lse
+    assert L.anchor_prefill_raw(pp, FAKE, FAKE, FAKE, None, None, None, FAKE, ws_ap, None) == K.ERR_INVALID
+    assert L.anchor_decode_raw(p, FAKE, FAKE, FAKE, None, None, None, FAKE, ws_ad, None) == K.ERR_INVALID
+    assert L.anchor_prefill_raw(pp, FAKE, FAKE, None, FAKE, None, None, FAKE, ws_ap, None) == K.ERR_INVALID
+    assert L.anchor_decode_raw(p, FAKE, FAKE, FAKE, FAKE, None, FAKE + 1, FAKE, ws_ad, None) == K.ERR_INVALID
     assert L.anchor_prefill_raw(pp, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, ws_ap - 256, None) == K.ERR_WORKSPACE
     assert L.reuse_prefill_raw(pp, FAKE, FAKE, None, FAKE, FAKE, None, 0, None) == K.ERR_INVALID
     assert L.reuse_prefill_raw(_prefill(dtype=K.F32), FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == K.ERR_UNSUPPORTED

@@ -16,6 +16,7 @@ from long_context_amd.synth import to_oracle  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
+BF16 = torch.bfloat16
 
 
 def _small(name, **kw):
@@ -39,6 +40,14 @@ CASES = {
     # a ragged last chunk: (chunk, head) score rows straddle store instructions.
     "bf16_g3_ragged": _small("bf16_g3_ragged", wid=908, hq=6, hkv=2, n=2021, k=200),
     "bf16_g6_d64": _small("bf16_g6_d64", wid=909, hq=12, hkv=2, d=64, n=1111, k=77),
+    # Long lists over few (batch, KV head) units: the reuse gather spreads a
+    # unit over several workgroups whose partials the last one to finish
+    # merges, and the last workgroup holds wavefronts with no entries.
+    "bf16_many_workgroups": _small("bf16_many_workgroups", wid=915, batch=1, hq=4, hkv=1, n=9000, k=4000),
+    "bf16_g16_d64_many_workgroups": _small("bf16_g16_d64_many_workgroups", wid=916, batch=1, hq=16, hkv=1,
+                                           d=64, n=5000, k=2500),
+    "bf16_g3_many_workgroups": _small("bf16_g3_many_workgroups", wid=917, batch=2, hq=6, hkv=2, n=7000,
+                                      k=3001),
 }
 
 
@@ -126,50 +135,55 @@ def test_decode_deterministic(lib):
     assert torch.equal(a[0], a[1]) and torch.equal(o[0], o[1])
 
 
-def _sampled_full(orc, w, units, seed):
-    """Full-size decode workload, drawn on the GPU; oracle checks on sampled (b, kv)."""
-    pos = synth.planted_positions(w.scaled(layers=2))
-    q0, k0, v0 = synth.make_layer(w, 0, DEV, pos)
-    q1, k1, v1 = synth.make_layer(w, 1, DEV, pos)
+def _full_workload(orc, w):
+    """Full-size decode workload, drawn on the GPU, checked against the oracle
+    on every unit: the anchor's index band, dense output and lse for all
+    B*Hkv (batch, KV head) units, then every query row of each reuse layer
+    (own K/V, the anchor's GPU index sets) against the oracle's reuse over
+    the same sets. Layers are drawn one at a time to bound memory."""
     G = w.group
+    pos = synth.planted_positions(w)
+    q0, k0, v0 = synth.make_layer(w, 0, DEV, pos)
     out = torch.empty_like(q0)
     lse = torch.empty((w.batch, w.hq, 1), dtype=torch.float32, device=DEV)
     idx = K.anchor_decode(q0, k0, v0, w.k, out=out, lse=lse)
     torch.cuda.synchronize()
     gi = idx.cpu().numpy()
-    out_h, lse_h = host64(out), host64(lse)
-    rng = np.random.default_rng(seed)
-    idx_r = random_index_sets(rng, (w.batch, w.hkv, 1), w.n, w.k)
-    refs = {}
-    for (b, kv) in units:
-        qs, ks, vs = (to_oracle(q0[b:b + 1, kv * G:(kv + 1) * G]), to_oracle(k0[b:b + 1, kv:kv + 1]),
-                      to_oracle(v0[b:b + 1, kv:kv + 1]))
-        io, po = orc.anchor_decode(qs, ks, w.k)
-        check_index_band(gi[b, kv, 0], io[0], po[0], w.k, w.n, f"{w.name} anchor ({b},{kv})")
-        do, lo = orc.dense(qs, ks, vs, causal=False)
-        check_close(out_h[b, kv * G:(kv + 1) * G, 0], do, w.torch_dtype, f"{w.name} dense ({b},{kv})")
-        check_lse(lse_h[b, kv * G:(kv + 1) * G, 0], lo, f"{w.name} lse ({b},{kv})")
-        idx_r[b, kv, 0] = io[0]
-        refs[(b, kv)] = (io[0], (to_oracle(q1[b:b + 1, kv * G:(kv + 1) * G]),
-                                 to_oracle(k1[b:b + 1, kv:kv + 1]), to_oracle(v1[b:b + 1, kv:kv + 1])))
-    out_r = K.reuse_decode(q1, k1, v1, torch.from_numpy(idx_r).to(DEV))
-    torch.cuda.synchronize()
-    out_rh = host64(out_r)
-    for (b, kv), (io, (qs, ks, vs)) in refs.items():
-        ro = orc.reuse_decode(qs, ks, vs, io.reshape(1, 1, 1, -1))
-        check_close(out_rh[b, kv * G:(kv + 1) * G, 0], ro, w.torch_dtype, f"{w.name} reuse ({b},{kv})")
+    Q0, K0, V0 = to_oracle(q0), to_oracle(k0), to_oracle(v0)
+    del q0, k0, v0
+    units = w.batch * w.hkv
+    log(f"[decode] {w.name}: oracle anchor over all {units} (batch, KV head) units")
+    io, po = orc.anchor_decode(Q0, K0, w.k)
+    flat = gi.reshape(-1, w.k)
+    same = sum(check_index_band(flat[u], io[u], po[u], w.k, w.n, f"{w.name} anchor unit {u}")
+               for u in range(units))
+    del po
+    do, lo = orc.dense(Q0, K0, V0, causal=False)
+    check_close(host64(out).reshape(-1, w.d), do, w.torch_dtype, f"{w.name} dense out")
+    check_lse(host64(lse).reshape(-1), lo, f"{w.name} lse")
+    log(f"[decode] {w.name}: anchor checked on {units} of {units} units ({same} index sets identical, "
+        f"the rest within the band), dense output and lse on {w.batch * w.hq} of {w.batch * w.hq} rows")
+    del Q0, K0, V0
+    for layer in range(1, w.layers):
+        q, k, v = synth.make_layer(w, layer, DEV, pos)
+        o = K.reuse_decode(q, k, v, idx)
+        torch.cuda.synchronize()
+        ro = orc.reuse_decode(to_oracle(q), to_oracle(k), to_oracle(v), gi)
+        check_close(host64(o).reshape(-1, w.d), ro, w.torch_dtype, f"{w.name} reuse layer {layer}")
+        log(f"[decode] {w.name}: reuse layer {layer} checked on {w.batch * w.hq} of {w.batch * w.hq} rows")
+        del q, k, v, o
 
 
-def test_decode_llama8b_32k_sampled(lib, orc):
+def test_decode_llama8b_32k_full(lib, orc):
     w = synth.WORKLOADS["decode_llama8b_32k"]
-    log("[decode] case=decode_llama8b_32k full size, sampled units")
-    _sampled_full(orc, w, [(0, 0), (5, 3), (11, 6), (15, 7)], seed=21)
+    log("[decode] case=decode_llama8b_32k full size, every unit and every reuse layer")
+    _full_workload(orc, w)
 
 
-def test_decode_128k_sampled(lib, orc):
+def test_decode_128k_full(lib, orc):
     w = synth.WORKLOADS["decode_128k"]
-    log("[decode] case=decode_128k full size, sampled units")
-    _sampled_full(orc, w, [(0, 0), (1, 5), (3, 7)], seed=22)
+    log("[decode] case=decode_128k full size, every unit and every reuse layer")
+    _full_workload(orc, w)
 
 
 def test_graph_replay_matches_eager(lib):
@@ -248,3 +262,43 @@ def test_decode_long_segments_against_oracle(lib, orc, n, k):
         check_index_band(gi[u], io[u], po[u], k, n, f"long n={n} k={k} unit {u}")
     if k == n:
         assert np.array_equal(gi, np.tile(np.arange(n, dtype=np.int32), (gi.shape[0], 1)))
+
+
+@pytest.mark.parametrize("case", ["bf16_d128_ragged", "f32_d128_g2", "bf16_g16"])
+def test_decode_dense_only(lib, orc, case):
+    """The anchor call without an index buffer is dense attention: output and
+    lse against the oracle's dense attention, and no index buffer is touched."""
+    w = CASES[case]
+    log(f"[decode] case=dense_only {case}")
+    (q, k, v), _ = _layers(w)
+    out = torch.empty_like(q, device=DEV)
+    lse = torch.empty((w.batch, w.hq, 1), dtype=torch.float32, device=DEV)
+    assert K.anchor_decode(q.to(DEV), k.to(DEV), v.to(DEV), w.k, out=out, lse=lse, dense_only=True) is None
+    torch.cuda.synchronize()
+    do, lo = orc.dense(to_oracle(q), to_oracle(k), to_oracle(v), causal=False)
+    check_close(host64(out).reshape(-1, w.d), do, w.torch_dtype, f"{case} dense-only out")
+    check_lse(host64(lse).reshape(-1), lo, f"{case} dense-only lse")
+    lse2 = torch.empty_like(lse)
+    K.anchor_decode(q.to(DEV), k.to(DEV), None, w.k, lse=lse2, dense_only=True)
+    torch.cuda.synchronize()
+    check_lse(host64(lse2).reshape(-1), lo, f"{case} dense-only lse without output")
+
+
+def test_decode_reuse_one_workspace_many_calls(lib, orc):
+    """One decode workspace, zero-filled once, serves reuse calls of different
+    sizes in a row (the arrival counters the gather's merge uses go back to
+    zero after every call), interleaved with an anchor call on the same
+    workspace; every output against the oracle."""
+    log("[decode] case=one_workspace_many_calls")
+    big = _small("ws_big", wid=918, batch=2, hq=8, hkv=2, n=9000, k=4000)
+    small = _small("ws_small", wid=919, batch=1, hq=8, hkv=2, n=3000, k=700)
+    ws = K.workspace(K.problem(torch.empty((2, 8, 1, 128), dtype=BF16), torch.empty((2, 2, 9000, 128), dtype=BF16),
+                               4000, 1), K.OP_ANCHOR_DECODE, DEV)
+    for w in (big, small, big, small):
+        (q0, k0, v0), (q1, k1, v1) = _layers(w)
+        idx = K.anchor_decode(q0.to(DEV), k0.to(DEV), None, w.k, ws=ws)
+        out = K.reuse_decode(q1.to(DEV), k1.to(DEV), v1.to(DEV), idx, ws=ws)
+        torch.cuda.synchronize()
+        ref = orc.reuse_decode(to_oracle(q1), to_oracle(k1), to_oracle(v1), idx.cpu().numpy())
+        check_close(host64(out).reshape(-1, w.d), ref, BF16, f"{w.name} reuse on a shared workspace")
+    assert not ws[:256].any(), "arrival counters left non-zero"

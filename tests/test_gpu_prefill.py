@@ -7,8 +7,7 @@ import pytest
 import torch
 
 sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
-from parity import (check_close, check_index_band, check_lse, host64, log,  # noqa: E402
-                    random_index_sets)
+from parity import check_close, check_index_band, check_lse, host64, log  # noqa: E402
 
 from long_context_amd import kascade as K  # noqa: E402
 from long_context_amd import synth  # noqa: E402
@@ -119,65 +118,113 @@ def test_prefill_deterministic(lib):
     assert torch.equal(a[0], a[1]) and torch.equal(o[0], o[1])
 
 
-def _sampled_full(orc, w, tiles_sample, n_rows, seed):
-    """Full-size prefill workload on the GPU; oracle on sampled tiles and rows."""
+def _anchor_tiles(w, per_kv, seed):
+    """(KV head, tile) pairs for the anchor check: per_kv tiles of every KV
+    head, seeded, each KV head including the first tile (even heads) or the
+    last one (odd heads). per_kv=None takes every tile."""
+    tiles = _tiles(w)
+    if per_kv is None or per_kv >= tiles:
+        return [(kv, t) for kv in range(w.hkv) for t in range(tiles)]
+    rng = np.random.default_rng(seed)
+    pairs = []
+    for kv in range(w.hkv):
+        forced = 0 if kv % 2 == 0 else tiles - 1
+        rest = rng.choice(np.setdiff1d(np.arange(tiles), [forced]), per_kv - 1, replace=False)
+        pairs += [(kv, int(t)) for t in sorted([forced, *rest.tolist()])]
+    return pairs
+
+
+def _full_workload(orc, w, per_kv, row_frac, seed):
+    """Full-size prefill workload on the GPU against the oracle:
+      * anchor index band on the (KV head, tile) pairs of _anchor_tiles;
+      * dense output and lse on a seeded row_frac share of the (head, row) rows;
+      * each reuse layer (own K/V, the anchor's GPU index sets) on a seeded
+        row_frac share of the rows plus 4 rows per head of every checked tile,
+        against the oracle's reuse over the same sets."""
     T, tiles, G = w.tile, _tiles(w), w.group
-    pos = synth.planted_positions(w.scaled(layers=2))
+    pos = synth.planted_positions(w)
     q0, k0, v0 = synth.make_layer(w, 0, DEV, pos)
-    q1, k1, v1 = synth.make_layer(w, 1, DEV, pos)
     out = torch.empty_like(q0)
     lse = torch.empty((w.batch, w.hq, w.n), dtype=torch.float32, device=DEV)
     idx = K.anchor_prefill(q0, k0, v0, w.k, T, out=out, lse=lse)
     torch.cuda.synchronize()
     gi = idx.cpu().numpy()
     Q0, K0, V0 = to_oracle(q0), to_oracle(k0), to_oracle(v0)
-    units = np.array([(0, kv, t) for kv, t in tiles_sample], np.int32)
-    io, po = orc.anchor_prefill(Q0, K0, w.k, T, units=units)
+    oh, lh = host64(out), host64(lse)
+    del q0, k0, v0, out, lse
+    pairs = _anchor_tiles(w, per_kv, seed)
+    log(f"[prefill] {w.name}: oracle anchor over {len(pairs)} of {w.hkv * tiles} (KV head, tile) pairs")
+    units = np.array([(0, kv, t) for kv, t in pairs], np.int32)
+    io, po = orc.anchor_prefill(Q0, K0, w.k, T, units=units, want_pooled=True)
+    same = 0
     for u, (_, kv, t) in enumerate(units):
         prefix = min((t + 1) * T, w.n)
-        check_index_band(gi[0, kv, t], io[u], po[u], min(w.k, prefix), prefix, f"{w.name} (kv{kv},t{t})")
-    rng = np.random.default_rng(seed)
-    rows = np.stack([np.zeros(n_rows, int), rng.integers(0, w.hq, n_rows), rng.integers(0, w.n, n_rows)], 1)
-    rows = rows.astype(np.int32)
-    drows = rows[:2048]
-    do, lo = orc.dense(Q0, K0, V0, causal=True, units=drows)
-    oh, lh = host64(out), host64(lse)
-    check_close(oh[drows[:, 0], drows[:, 1], drows[:, 2]], do, BF16, f"{w.name} dense rows")
-    check_lse(lh[drows[:, 0], drows[:, 1], drows[:, 2]], lo, f"{w.name} lse rows")
-    # reuse: sampled tiles carry the oracle's sets, the rest seeded random sets
-    prefixes = np.minimum((np.arange(tiles) + 1) * T, w.n)
-    idx_r = random_index_sets(rng, (1, w.hkv, tiles), np.broadcast_to(prefixes, (1, w.hkv, tiles)), w.k)
-    for u, (_, kv, t) in enumerate(units):
-        idx_r[0, kv, t] = io[u]
-    out_r = K.reuse_prefill(q1, k1, v1, torch.from_numpy(idx_r).to(DEV), T)
-    torch.cuda.synchronize()
-    ro = orc.reuse_prefill(to_oracle(q1), to_oracle(k1), to_oracle(v1), idx_r, T, units=rows)
-    check_close(host64(out_r)[rows[:, 0], rows[:, 1], rows[:, 2]], ro, BF16, f"{w.name} reuse rows")
-    # rows of the sampled tiles specifically
+        kt = min(w.k, prefix)
+        same += check_index_band(gi[0, kv, t], io[u], po[u], kt, prefix, f"{w.name} (kv{kv},t{t})")
+        if kt == prefix:
+            assert gi[0, kv, t, :kt].tolist() == list(range(prefix)), f"{w.name} tile {t} keeps everything"
+    del po
+    log(f"[prefill] {w.name}: anchor checked on {len(pairs)} (KV head, tile) pairs ({same} index sets "
+        f"identical, the rest within the band)")
+    rng = np.random.default_rng(seed + 1)
+    total_rows = w.hq * w.n
+    n_rows = max(1, int(round(row_frac * total_rows)))
+    flat = np.sort(rng.choice(total_rows, n_rows, replace=False))
+    rows = np.stack([np.zeros(n_rows, np.int64), flat // w.n, flat % w.n], 1).astype(np.int32)
+    do, lo = orc.dense(Q0, K0, V0, causal=True, units=rows)
+    check_close(oh[rows[:, 0], rows[:, 1], rows[:, 2]], do, BF16, f"{w.name} dense rows")
+    check_lse(lh[rows[:, 0], rows[:, 1], rows[:, 2]], lo, f"{w.name} lse rows")
+    log(f"[prefill] {w.name}: dense output and lse checked on {n_rows} of {total_rows} rows")
+    del Q0, K0, V0, oh, lh
     trows = []
     for (_, kv, t) in units:
         for h in range(kv * G, (kv + 1) * G):
-            for i in rng.choice(np.arange(t * T, min((t + 1) * T, w.n)), 4, replace=False):
-                trows.append((0, h, i))
-    trows = np.array(trows, np.int32)
-    ro = orc.reuse_prefill(to_oracle(q1), to_oracle(k1), to_oracle(v1), idx_r, T, units=trows)
-    check_close(host64(out_r)[trows[:, 0], trows[:, 1], trows[:, 2]], ro, BF16, f"{w.name} reuse tile rows")
+            for i in rng.choice(np.arange(t * T, min((t + 1) * T, w.n)), min(4, w.n - t * T), replace=False):
+                trows.append((0, h, int(i)))
+    rrows = np.concatenate([rows, np.array(trows, np.int32).reshape(-1, 3)])
+    for layer in range(1, w.layers):
+        q, k, v = synth.make_layer(w, layer, DEV, pos)
+        o = K.reuse_prefill(q, k, v, idx, T)
+        torch.cuda.synchronize()
+        ro = orc.reuse_prefill(to_oracle(q), to_oracle(k), to_oracle(v), gi, T, units=rrows)
+        check_close(host64(o)[rrows[:, 0], rrows[:, 1], rrows[:, 2]], ro, BF16, f"{w.name} reuse layer {layer}")
+        log(f"[prefill] {w.name}: reuse layer {layer} checked on {len(rrows)} rows "
+            f"({n_rows} seeded, {len(trows)} in the checked tiles)")
+        del q, k, v, o
 
 
-def test_prefill_8k_sampled(lib, orc):
+def test_prefill_8k_full(lib, orc):
+    """Every (KV head, tile) anchor set of the 8K workload; 1/8 of the rows."""
     w = synth.WORKLOADS["prefill_8k"]
-    log("[prefill] case=prefill_8k full size, sampled tiles and rows")
-    _sampled_full(orc, w, [(0, 0), (0, 7), (3, 8), (5, 31), (7, 63)], 2048, seed=31)
+    log("[prefill] case=prefill_8k full size, every anchor tile")
+    _full_workload(orc, w, per_kv=None, row_frac=1 / 8, seed=31)
 
 
 def test_prefill_8k_t64_sampled(lib, orc):
     w = synth.WORKLOADS["prefill_8k"].scaled(tile=64)
     log("[prefill] case=prefill_8k with 64-row tiles, sampled tiles and rows")
-    _sampled_full(orc, w, [(0, 0), (1, 15), (3, 16), (5, 63), (7, 127)], 2048, seed=33)
+    _full_workload(orc, w, per_kv=6, row_frac=1 / 64, seed=33)
 
 
 def test_prefill_32k_sampled(lib, orc):
+    """A seeded 1 % of the rows (the workload's own sample size) and 8 anchor
+    tiles per KV head, the first and the last tile among them."""
     w = synth.WORKLOADS["prefill_32k"]
-    log("[prefill] case=prefill_32k full size, sampled tiles and 1% of rows")
-    n_rows = (w.hq * w.n) // 100
-    _sampled_full(orc, w, [(0, 0), (2, 15), (4, 100), (6, 200), (7, 255)], n_rows, seed=32)
+    log("[prefill] case=prefill_32k full size, 64 anchor tiles and 1% of rows")
+    _full_workload(orc, w, per_kv=8, row_frac=1 / 100, seed=32)
+
+
+@pytest.mark.parametrize("case", ["d128_ragged", "d64_g8", "n1"])
+def test_prefill_dense_only(lib, orc, case):
+    """The anchor call without an index buffer is dense causal attention."""
+    w = CASES[case]
+    log(f"[prefill] case=dense_only {case}")
+    (q, k, v), _ = synth.make_stack(w, device="cpu")
+    out = torch.empty_like(q, device=DEV)
+    lse = torch.empty((w.batch, w.hq, w.n), dtype=torch.float32, device=DEV)
+    assert K.anchor_prefill(q.to(DEV), k.to(DEV), v.to(DEV), w.k, w.tile, out=out, lse=lse,
+                            dense_only=True) is None
+    torch.cuda.synchronize()
+    do, lo = orc.dense(to_oracle(q), to_oracle(k), to_oracle(v), causal=True)
+    check_close(host64(out).reshape(-1, w.d), do, BF16, f"{case} dense-only out")
+    check_lse(host64(lse).reshape(-1), lo, f"{case} dense-only lse")
