@@ -82,7 +82,9 @@ typedef enum {
   KASCADE_ERR_INVALID = 1,     /* inconsistent shape or argument, null or misaligned pointer */
   KASCADE_ERR_UNSUPPORTED = 2, /* well-formed but not provided (head_dim, dtype, tile size) */
   KASCADE_ERR_WORKSPACE = 3,   /* workspace null or smaller than kascade_workspace_bytes() */
-  KASCADE_ERR_HIP = 4          /* a HIP launch or runtime call failed */
+  KASCADE_ERR_HIP = 4,         /* a HIP launch or runtime call failed */
+  KASCADE_ERR_SCRATCH = 5      /* kascade_reuse_decode_noalloc: the problem needs more scratch
+                                  than the library's array holds (KASCADE_NOALLOC_SCRATCH_BYTES) */
 } kascade_status;
 
 typedef enum { KASCADE_F32 = 0, KASCADE_BF16 = 1 } kascade_dtype;
@@ -150,6 +152,23 @@ int kascade_anchor_decode(const kascade_problem* p, const void* q, const void* k
 int kascade_reuse_decode(const kascade_problem* p, const void* q, const void* k,
                          const void* v, const int32_t* idx, void* out,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Reuse layer, decode, allocating nothing: for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation). Same computation, arguments and results as
+ * kascade_reuse_decode, without the workspace: the scratch is a device array
+ * inside the library of KASCADE_NOALLOC_SCRATCH_BYTES bytes, one per GPU,
+ * kept until the process ends. The first call on a GPU looks up that array's
+ * address and clears it with a kernel on `stream`; make that first call
+ * outside graph capture if the lookup must not happen during capture.
+ * Returns KASCADE_ERR_SCRATCH, before anything is enqueued, for a problem
+ * whose kascade_workspace_bytes(p, KASCADE_OP_REUSE_DECODE) exceeds the
+ * array. Every call on a GPU shares that GPU's array: calls that may overlap
+ * on one GPU (other streams, other host threads) race and must be serialised
+ * by the caller. */
+#define KASCADE_NOALLOC_SCRATCH_BYTES (8u << 20)
+int kascade_reuse_decode_noalloc(const kascade_problem* p, const void* q, const void* k,
+                                 const void* v, const int32_t* idx, void* out, void* stream);
 
 /* Anchor layer, causal prefill. Defined by: exact top-k selection in the
  * anchor layer, done per query tile in prefill (Kascade abstract, opentrain.ai

@@ -7,6 +7,7 @@
 #include <mutex>
 #include <vector>
 
+#include "api_internal.hpp"
 #include "kascade.h"
 #include "kernels.hpp"
 
@@ -288,6 +289,36 @@ PrefillArgs prefill_args(const kascade_problem* p, const void* q, const void* k,
 
 }  // namespace
 
+namespace kascade {
+
+int reuse_decode_check(const kascade_problem* p, const void* q, const void* k, const void* v,
+                       const int32_t* idx, const void* out) {
+  const int rc = validate(p, KASCADE_OP_REUSE_DECODE);
+  if (rc) return rc;
+  if (!q || !k || !v || !idx || !out) return KASCADE_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned4(idx))
+    return KASCADE_ERR_INVALID;
+  return KASCADE_OK;
+}
+
+int reuse_decode_enqueue(const kascade_problem* p, const void* q, const void* k, const void* v,
+                         const int32_t* idx, void* out, char* ws, hipStream_t s) {
+  const DecodeWorkspace w = decode_workspace(p, KASCADE_OP_REUSE_DECODE);
+  DecodeArgs a = decode_args(p, q, k, v, idx, w, ws);
+  a.list_len = p->top_k;
+  a.out = out;
+  if (w.merged) {
+    KASCADE_TRY("decode_attn_gather", launch_decode_gather_merged(a, s));
+    return KASCADE_OK;
+  }
+  KASCADE_TRY("decode_attn_gather", launch_decode_attn(a, false, true, true, s));
+  KASCADE_TRY("decode_combine", launch_decode_combine(a.part_ml, a.part_o, p->batch * a.hq,
+                                                      a.splits, a.d, false, out, nullptr, nullptr, s));
+  return KASCADE_OK;
+}
+
+}  // namespace kascade
+
 extern "C" {
 
 int kascade_validate(const kascade_problem* p, int op) { return validate(p, op); }
@@ -301,6 +332,7 @@ const char* kascade_status_string(int status) {
     case KASCADE_ERR_UNSUPPORTED: return "unsupported problem";
     case KASCADE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case KASCADE_ERR_HIP: return "HIP launch or runtime error";
+    case KASCADE_ERR_SCRATCH: return "problem exceeds the allocation-free entry point's scratch";
     default: return "unknown status";
   }
 }
@@ -353,26 +385,12 @@ int kascade_anchor_decode(const kascade_problem* p, const void* q, const void* k
 int kascade_reuse_decode(const kascade_problem* p, const void* q, const void* k, const void* v,
                          const int32_t* idx, void* out, void* workspace, size_t workspace_bytes,
                          void* stream) {
-  int rc = validate(p, KASCADE_OP_REUSE_DECODE);
+  int rc = kascade::reuse_decode_check(p, q, k, v, idx, out);
   if (rc) return rc;
-  if (!q || !k || !v || !idx || !out) return KASCADE_ERR_INVALID;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned4(idx))
-    return KASCADE_ERR_INVALID;
   rc = check_workspace(p, KASCADE_OP_REUSE_DECODE, workspace, workspace_bytes);
   if (rc) return rc;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const DecodeWorkspace w = decode_workspace(p, KASCADE_OP_REUSE_DECODE);
-  DecodeArgs a = decode_args(p, q, k, v, idx, w, static_cast<char*>(workspace));
-  a.list_len = p->top_k;
-  a.out = out;
-  if (w.merged) {
-    KASCADE_TRY("decode_attn_gather", launch_decode_gather_merged(a, s));
-    return KASCADE_OK;
-  }
-  KASCADE_TRY("decode_attn_gather", launch_decode_attn(a, false, true, true, s));
-  KASCADE_TRY("decode_combine", launch_decode_combine(a.part_ml, a.part_o, p->batch * a.hq,
-                                                      a.splits, a.d, false, out, nullptr, nullptr, s));
-  return KASCADE_OK;
+  return kascade::reuse_decode_enqueue(p, q, k, v, idx, out, static_cast<char*>(workspace),
+                                       static_cast<hipStream_t>(stream));
 }
 
 int kascade_anchor_prefill(const kascade_problem* p, const void* q, const void* k, const void* v,

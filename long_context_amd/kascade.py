@@ -13,11 +13,13 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkascade.
 
 F32, BF16 = 0, 1
 OP_ANCHOR_DECODE, OP_REUSE_DECODE, OP_ANCHOR_PREFILL, OP_REUSE_PREFILL = 0, 1, 2, 3
-OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
+OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_SCRATCH = 0, 1, 2, 3, 4, 5
+NOALLOC_SCRATCH_BYTES = 8 << 20   # KASCADE_NOALLOC_SCRATCH_BYTES
 
 EXPORTS = ("kascade_validate", "kascade_workspace_bytes", "kascade_status_string",
-           "kascade_anchor_decode", "kascade_reuse_decode", "kascade_anchor_prefill",
-           "kascade_reuse_prefill", "kascade_timing_enable", "kascade_timing_collect")
+           "kascade_anchor_decode", "kascade_reuse_decode", "kascade_reuse_decode_noalloc",
+           "kascade_anchor_prefill", "kascade_reuse_prefill", "kascade_timing_enable",
+           "kascade_timing_collect")
 
 
 class KascadeError(RuntimeError):
@@ -69,6 +71,8 @@ class Library:
             f = getattr(lib, name)
             f.argtypes = args
             f.restype = ctypes.c_int
+        lib.kascade_reuse_decode_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp]
+        lib.kascade_reuse_decode_noalloc.restype = ctypes.c_int
         lib.kascade_timing_enable.argtypes = [ctypes.c_int]
         lib.kascade_timing_enable.restype = ctypes.c_int
         lib.kascade_timing_collect.argtypes = [ctypes.POINTER(KernelTime), ctypes.c_int]
@@ -109,6 +113,9 @@ class Library:
     def reuse_decode_raw(self, prob, q, k, v, idx, out, ws, ws_bytes, stream):
         return self.lib.kascade_reuse_decode(ctypes.byref(prob), q, k, v, idx, out, ws, ws_bytes,
                                              stream)
+
+    def reuse_decode_noalloc_raw(self, prob, q, k, v, idx, out, stream):
+        return self.lib.kascade_reuse_decode_noalloc(ctypes.byref(prob), q, k, v, idx, out, stream)
 
     def anchor_prefill_raw(self, prob, q, k, v, out, idx, lse, ws, ws_bytes, stream):
         return self.lib.kascade_anchor_prefill(ctypes.byref(prob), q, k, v, out, idx, lse, ws,
@@ -222,6 +229,19 @@ def reuse_decode(q, k, v, idx, out=None, ws=None, scale=0.0, stream=None, shared
     wp, wb = _ws(ws)
     lib.check(lib.reuse_decode_raw(prob, _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(out), wp, wb,
                                    _stream(stream)), "kascade_reuse_decode")
+    return out
+
+
+def reuse_decode_noalloc(q, k, v, idx, out=None, scale=0.0, stream=None, shared=False):
+    """Reuse decode through the allocation-free entry point (library-held
+    scratch, no workspace); returns out [B,Hq,1,d]."""
+    lib = library()
+    prob = problem(q, k, idx.shape[-1], 1, scale, shared)
+    _check_idx(idx, prob, "reuse_decode_noalloc")
+    if out is None:
+        out = torch.empty_like(q)
+    lib.check(lib.reuse_decode_noalloc_raw(prob, _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(out),
+                                           _stream(stream)), "kascade_reuse_decode_noalloc")
     return out
 
 

@@ -114,7 +114,7 @@ def test_workspace_sizes(L):
 
 
 def test_status_strings(L):
-    for s in (K.OK, K.ERR_INVALID, K.ERR_UNSUPPORTED, K.ERR_WORKSPACE, K.ERR_HIP):
+    for s in (K.OK, K.ERR_INVALID, K.ERR_UNSUPPORTED, K.ERR_WORKSPACE, K.ERR_HIP, K.ERR_SCRATCH):
         assert L.status_string(s) and L.status_string(s) != "unknown status"
     assert L.status_string(99) == "unknown status"
 
@@ -187,3 +187,17 @@ def test_binding_checks_index_set_shape():
     with pytest.raises(ValueError, match="idx must be int32"):
         K.reuse_prefill(qp, kp, kp, torch.zeros((1, 2, 2, 16), dtype=torch.int32))         # 3 tiles expected
     assert K.idx_shape(K.problem(qp, kp, 16, 128, shared=True)) == (1, 1, 3, 16)
+
+
+def test_noalloc_rejects_before_launch(L):
+    """The allocation-free reuse decode refuses, on the host, a problem whose
+    workspace exceeds its scratch, and the usual argument errors."""
+    big = _prob(batch=512, num_q_heads=32, num_kv_heads=8, kv_len=32768, top_k=2048)
+    assert L.workspace_bytes(big, K.OP_REUSE_DECODE) > K.NOALLOC_SCRATCH_BYTES
+    assert L.reuse_decode_noalloc_raw(big, FAKE, FAKE, FAKE, FAKE, FAKE, None) == K.ERR_SCRATCH
+    p = _prob()
+    assert L.workspace_bytes(p, K.OP_REUSE_DECODE) <= K.NOALLOC_SCRATCH_BYTES
+    assert L.reuse_decode_noalloc_raw(_prob(num_q_heads=6, num_kv_heads=4), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                      None) == K.ERR_INVALID
+    assert L.reuse_decode_noalloc_raw(p, FAKE, FAKE, None, FAKE, FAKE, None) == K.ERR_INVALID
+    assert L.reuse_decode_noalloc_raw(p, FAKE, FAKE, FAKE, FAKE + 1, FAKE, None) == K.ERR_INVALID
