@@ -308,6 +308,84 @@ def profile_pass(kind, reps, workloads=("decode_llama8b_32k", "prefill_8k")):
     print(json.dumps({"profile_pass": "kernels", "reps": reps, "workloads": list(workloads)}), flush=True)
 
 
+def probe_gather(reps=5, workload="decode_llama8b_32k"):
+    """Cold-cache memory ceiling of the decode reuse layer's access pattern.
+
+    A load-only probe (long_context_amd/csrc/probe/gather_probe.hip) reads the
+    K and V rows that the anchor's index sets name -- the reuse gather's bytes
+    without its arithmetic -- and the same number of rows read contiguously,
+    over a sweep of wavefronts per (batch, KV head) and of row groups in
+    flight per wavefront. Before every timed launch a 2 GiB buffer is read,
+    which fills the 256 MB Infinity Cache with unrelated clean lines (a
+    written flush would leave dirty lines to be written back during the timed
+    kernel). The reuse call itself is timed the same way. Times are HIP events
+    around the one launch; under rocprofv3 --kernel-trace the dispatches give
+    the kernel durations alone. One JSON line per configuration, then a
+    summary line."""
+    import ctypes
+    from long_context_amd import build as B
+    lib = ctypes.CDLL(B.PROBE_LIBRARY)
+    lib.kascade_probe_gather.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 6 + [ctypes.c_void_p] * 2
+    lib.kascade_probe_gather.restype = ctypes.c_int
+    dev = "cuda"
+    w = synth.WORKLOADS[workload].scaled(layers=2)
+    pos = synth.planted_positions(w)
+    q0, k0, _ = synth.make_layer(w, 0, dev, pos)
+    q1, k1, v1 = synth.make_layer(w, 1, dev, pos)
+    idx = K.anchor_decode(q0, k0, None, w.k)
+    del q0, k0
+    units = w.batch * w.hkv
+    assert w.d == 128 and k1.dtype == torch.bfloat16  # 256-byte rows
+    flush = torch.ones((2 << 30) // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    gather_bytes = units * w.k * w.d * 2 * 2
+
+    def cold(launch):
+        times = []
+        for _ in range(reps):
+            flush.sum()
+            torch.cuda.synchronize()
+            a, b = _event(), _event()
+            a.record()
+            launch()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b) * 1e3)
+        return float(np.median(times))
+
+    out = torch.empty_like(q1)
+    ws = K.workspace(K.problem(q1, k1, w.k, 1), K.OP_REUSE_DECODE, dev)
+    t_reuse = cold(lambda: K.reuse_decode(q1, k1, v1, idx, out=out, ws=ws))
+    rows = []
+    for contiguous in (0, 1):
+        for splits in (8, 16, 32, 64):
+            for inflight in (1, 2, 4, 8):
+                def launch():
+                    rc = lib.kascade_probe_gather(k1.data_ptr(), v1.data_ptr(), idx.data_ptr(), units, w.n, w.k,
+                                                  splits, inflight, contiguous, sink.data_ptr(), stream)
+                    assert rc == 0, rc
+                t = cold(launch)
+                row = {"probe": "gather_ceiling", "workload": w.name, "rows": "contiguous" if contiguous else "gathered",
+                       "waves_per_unit": splits, "row_groups_in_flight": inflight, "us": round(t, 2),
+                       "gbs": round(gather_bytes / (t * 1e-6) / 1e9, 1)}
+                rows.append(row)
+                print(json.dumps(row), flush=True)
+    best = {kind: max((r for r in rows if r["rows"] == kind), key=lambda r: r["gbs"]) for kind in ("gathered", "contiguous")}
+    print(json.dumps({"probe": "gather_ceiling_summary", "workload": w.name, "bytes": gather_bytes,
+                      "reuse_call_cold_us": round(t_reuse, 2),
+                      "reuse_call_cold_gbs": round(dec_reuse_bytes(w) / (t_reuse * 1e-6) / 1e9, 1),
+                      "best_gathered": best["gathered"], "best_contiguous": best["contiguous"],
+                      "peak_gbs": PEAK_HBM_GBS}), flush=True)
+
+
+def dec_reuse_bytes(w):
+    """Algorithmic bytes of one decode reuse layer: gathered K and V rows, idx, Q and O."""
+    esz = 4 if w.dtype == "f32" else 2
+    return (w.batch * w.hkv * w.k * w.d * esz * 2 + w.batch * w.hkv * w.k * 4
+            + 2 * w.batch * w.hq * w.d * esz)
+
+
 # ---- accuracy against dense attention, swept over k -------------------------
 #
 # The pages leave k as a hyper-parameter picked with a small validation sweep
@@ -456,6 +534,9 @@ def main():
                     help="run a short pass for rocprofv3 counters instead of the benchmark")
     ap.add_argument("--profile-workloads", default="decode_llama8b_32k,prefill_8k",
                     help="comma-separated synthetic workloads for --profile-pass kernels")
+    ap.add_argument("--probe", choices=("gather",),
+                    help="cold-cache memory ceiling of the decode reuse gather (load-only probe sweep)")
+    ap.add_argument("--probe-workload", default="decode_llama8b_32k")
     ap.add_argument("--sweep", action="store_true",
                     help="accuracy against dense attention over k = N/64 ... N/4 (one JSON line per k)")
     args = ap.parse_args()
@@ -468,6 +549,9 @@ def main():
         sys.exit(2)
     if args.profile_pass:
         profile_pass(args.profile_pass, max(args.steps, 1), tuple(args.profile_workloads.split(",")))
+        return
+    if args.probe == "gather":
+        probe_gather(workload=args.probe_workload)
         return
     if args.sweep:
         for w in sweep_workloads():

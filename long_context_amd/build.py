@@ -9,6 +9,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIBRARY = os.path.join(HERE, "libkascade.so")
+PROBE_LIBRARY = os.path.join(HERE, "libkascade_probe.so")  # measurement probes used by bench.py --probe
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -35,21 +36,29 @@ def _compile(src, build_dir=BUILD, defines=()):
     return obj
 
 
-def build(verbose=False, library=LIBRARY, build_dir=BUILD, defines=()):
-    """Compile every kernel source for gfx950 and link the shared library.
-
-    `defines` (NAME=VALUE strings) and a different `library` path build a
-    variant of the library with other compile-time settings."""
-    os.makedirs(build_dir, exist_ok=True)
-    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(sources))) as ex:
-        objs = list(ex.map(lambda src: _compile(src, build_dir, defines), sources))
+def _link(objs, library):
     tmp = library + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, library)
+
+
+def build(verbose=False, library=LIBRARY, build_dir=BUILD, defines=(), probe=True):
+    """Compile every kernel source for gfx950 and link the shared library, and
+    (probe=True) the measurement probe library next to it.
+
+    `defines` (NAME=VALUE strings) and a different `library` path build a
+    variant of the library with other compile-time settings."""
+    os.makedirs(build_dir, exist_ok=True)
+    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    probes = sorted(glob.glob(os.path.join(CSRC, "probe", "*.hip"))) if probe else []
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(sources) + len(probes))) as ex:
+        objs = list(ex.map(lambda src: _compile(src, build_dir, defines), sources + probes))
+    _link(objs[:len(sources)], library)
+    if probes:
+        _link(objs[len(sources):], PROBE_LIBRARY)
     if verbose:
         print(library)
     return library

@@ -69,17 +69,20 @@ struct DecodeSplit {
   int splits, keys_per_split;
 };
 
+#ifndef KASCADE_GATHER_GRAIN
+#define KASCADE_GATHER_GRAIN 64
+#endif
 // Spread a list of `len` keys per (b, KV head) over enough wavefronts to fill
-// the chip; each wavefront gets a multiple of 64 keys.
-DecodeSplit decode_split(const kascade_problem* p, int len, bool dense) {
+// the chip; each wavefront gets a multiple of `grain` keys.
+DecodeSplit decode_split(const kascade_problem* p, int len, bool dense, int grain = 64) {
   const int units = p->batch * p->num_kv_heads;
-  const int max_splits = (len + 63) / 64;
+  const int max_splits = (len + grain - 1) / grain;
   const int target = dense ? kTargetWavesDense : kTargetWaves;
   int splits = (target + units - 1) / units;
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;
   int kps = (len + splits - 1) / splits;
-  kps = (kps + 63) / 64 * 64;
+  kps = (kps + grain - 1) / grain * grain;
   return {(len + kps - 1) / kps, kps};
 }
 
@@ -92,7 +95,7 @@ struct DecodeWorkspace {
 // bf16 reuse decode fuses the split merge into the gather: the splits come in
 // workgroups of kGatherWaves wavefronts, and the partials are per workgroup.
 DecodeSplit gather_split(const kascade_problem* p) {
-  DecodeSplit s = decode_split(p, p->top_k, false);
+  DecodeSplit s = decode_split(p, p->top_k, false, KASCADE_GATHER_GRAIN);
   s.splits = (s.splits + kGatherWaves - 1) / kGatherWaves * kGatherWaves;
   return s;
 }
