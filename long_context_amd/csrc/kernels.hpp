@@ -109,6 +109,11 @@ struct PrefillArgs {
 hipError_t launch_prefill_dense(const PrefillArgs& a, hipStream_t s);   // pass 1: lse2 (+ out)
 hipError_t launch_prefill_pool(const PrefillArgs& a, hipStream_t s);    // pass 2: pooled
 hipError_t launch_prefill_reuse(const PrefillArgs& a, hipStream_t s);   // reuse attention
+// Reuse attention with the gathered rows loaded straight into a ring of LDS
+// buffers (d 64 or 128, tile 64 or 128, four wavefronts of 32 rows per
+// workgroup: one head at tile 128, two at tile 64, whose group must be even).
+bool prefill_reuse_ring_supported(const PrefillArgs& a);
+hipError_t launch_prefill_reuse_ring(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_lse2_to_lse(const float* lse2, float* lse, size_t count, hipStream_t s);
 
 }  // namespace kascade
