@@ -58,6 +58,7 @@ __global__ __launch_bounds__(64 * WAVES) void prefill_reuse_ring(PrefillArgs a) 
   constexpr int NH = WAVES / RB;      // heads per workgroup
   constexpr int QB = NH * TR * ROWB;  // bytes of the workgroup's query rows
   constexpr int QI = QB / 1024 / WAVES;  // 1-KB query loads per wavefront
+  static_assert((NB & (NB - 1)) == 0 && (KS & (KS - 1)) == 0, "ring sizes are powers of two");
   static_assert(QB == 4 * CB && NI >= 1 && QI >= 1 && QI < 64 && 4 * NI + 2 < 64 && KC % 32 == 0 && KC <= 64,
                 "staging shape");
   __shared__ __attribute__((aligned(1024))) unsigned char ks[NB][CB];
@@ -105,7 +106,7 @@ __global__ __launch_bounds__(64 * WAVES) void prefill_reuse_ring(PrefillArgs a) 
   // list repeat its last entry; the masks know the list length).
   auto issue_keys = [&](int x) __attribute__((always_inline)) {
     const int pos = min(x * KC + lane, list_len - 1);
-    lds_dma4_at(list, (unsigned)pos * 4u, lds_address(&keys_w[w][x % KS][0]));
+    lds_dma4_at(list, (unsigned)pos * 4u, lds_address(&keys_w[w][x & (KS - 1)][0]));
   };
   auto issue_pad = [&]() __attribute__((always_inline)) {
     lds_dma4_at(list, 0u, lds_address(&keys_w[w][KS][0]));
@@ -124,13 +125,13 @@ __global__ __launch_bounds__(64 * WAVES) void prefill_reuse_ring(PrefillArgs a) 
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
       const int rho = (w * NI + j) * RPI + lane / SLOTS;
-      const int key = keys_w[w][x % KS][rho];
+      const int key = keys_w[w][x & (KS - 1)][rho];
       const bool ok = x * KC + rho < list_len && (unsigned)key < (unsigned)a.n;
       off[j] = (ok ? (unsigned)key * (unsigned)ROWB : 0u) + slot_off[j];
     }
   };
   auto issue_rows = [&](int x, const unsigned (&off)[NI]) __attribute__((always_inline)) {
-    const int buf = x % NB;
+    const int buf = x & (NB - 1);
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
       lds_dma16_at(kb, off[j], lds_address(&ks[buf][(w * NI + j) * 1024]));
@@ -141,7 +142,7 @@ __global__ __launch_bounds__(64 * WAVES) void prefill_reuse_ring(PrefillArgs a) 
   // row of this wavefront must not see (above its first row, or outside the
   // sequence: unsigned compare).
   auto chunk_masked = [&](int x) __attribute__((always_inline)) -> bool {
-    const int key = keys_w[w][x % KS][lane];
+    const int key = keys_w[w][x & (KS - 1)][lane];
     return (x + 1) * KC > list_len || __any(lane < KC && (unsigned)key > (unsigned)wrow0);
   };
 
@@ -162,10 +163,11 @@ __global__ __launch_bounds__(64 * WAVES) void prefill_reuse_ring(PrefillArgs a) 
     const int last = a.n - 1 - row0;
 #pragma unroll
     for (int jq = 0; jq < QI; ++jq) {
-      const int o = (w * QI + jq) * 1024 + 16 * lane;
-      const int hh = o / (TR * ROWB), r = (o % (TR * ROWB)) / ROWB, p = (o % ROWB) / 16;
-      const unsigned off = (unsigned)(hh * a.n + min(r, last)) * (unsigned)ROWB + 16u * (unsigned)(p ^ swz<D>(r));
-      lds_dma16_at_nt(qb, off, lds_address(stage_at((w * QI + jq) * 1024)));
+      const unsigned o = (unsigned)(w * QI + jq) * 1024u + 16u * (unsigned)lane;
+      const unsigned hh = o / (TR * ROWB), r = (o % (TR * ROWB)) / ROWB, p = (o % ROWB) / 16;
+      const unsigned off = (hh * (unsigned)a.n + (unsigned)min((int)r, last)) * (unsigned)ROWB +
+                           16u * (p ^ (unsigned)swz<D>((int)r));
+      lds_dma16_at_nt(qb, off, lds_address(stage_at((int)(o & ~1023u))));
     }
   }
   wait_vm(QI);  // the entries of chunks 0..5 are in place
@@ -239,7 +241,7 @@ __global__ __launch_bounds__(64 * WAVES) void prefill_reuse_ring(PrefillArgs a) 
   auto apply_mask = [&](int j, f32x16& s) __attribute__((always_inline)) {
     const int c = j / SPC, sub = j % SPC;
     const int lim = list_len - c * KC;
-    const int* kr = &keys_w[w][c % KS][32 * sub + 4 * hf];
+    const int* kr = &keys_w[w][c & (KS - 1)][32 * sub + 4 * hf];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int4 k4 = *reinterpret_cast<const int4*>(kr + 8 * q);
@@ -261,7 +263,7 @@ __global__ __launch_bounds__(64 * WAVES) void prefill_reuse_ring(PrefillArgs a) 
   bool masked = advance(0);  // chunk 0
   read_k(0, 0, kf);
   for (int j = 0; j < nsteps; ++j) {
-    const int c = j / SPC, sub = j % SPC, buf = c % NB;
+    const int c = j / SPC, sub = j % SPC, buf = c & (NB - 1);
     read_v(buf, sub, vf);
     f32x16 s = zero_f32x16();
 #pragma unroll
@@ -271,7 +273,7 @@ __global__ __launch_bounds__(64 * WAVES) void prefill_reuse_ring(PrefillArgs a) 
     // the last step, K of ring rows that are not used).
     const int jn = j + 1;
     if (sub == SPC - 1 && c + 1 < nchunks) masked = advance(c + 1);
-    read_k((jn / SPC) % NB, jn % SPC, kf);
+    read_k((jn / SPC) & (NB - 1), jn % SPC, kf);
 
     float cmax = s[0];
 #pragma unroll
@@ -338,14 +340,17 @@ float lsum = 0.f;
       }
   }
   __syncthreads();
+  // Head hh's rows are contiguous from the workgroup's first: one uniform base,
+  // 32-bit lane offsets.
+  unsigned char* ob = reinterpret_cast<unsigned char*>(a.out + ((size_t)(b * a.hq + h0) * a.n + row0) * D);
 #pragma unroll
   for (int jq = 0; jq < QI; ++jq) {
-    const int o = (w * QI + jq) * 1024 + 16 * lane;
-    const int hh = o / (TR * ROWB), r = (o % (TR * ROWB)) / ROWB, p = (o % ROWB) / 16;
-    if (row0 + r < a.n) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(stage_at(o));  // eight bf16, moved as bits
-      __builtin_nontemporal_store(
-          v, reinterpret_cast<f32x4*>(a.out + ((size_t)(b * a.hq + h0 + hh) * a.n + row0 + r) * D + 8 * (p ^ swz<D>(r))));
+    const unsigned o = (unsigned)(w * QI + jq) * 1024u + 16u * (unsigned)lane;
+    const unsigned hh = o / (TR * ROWB), r = (o % (TR * ROWB)) / ROWB, p = (o % ROWB) / 16;
+    if (row0 + (int)r < a.n) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(stage_at((int)o));  // eight bf16, moved as bits
+      const unsigned off = (hh * (unsigned)a.n + r) * (unsigned)ROWB + 16u * (p ^ (unsigned)swz<D>((int)r));
+      __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(ob + off));
     }
   }
 }
