@@ -37,11 +37,12 @@ METRIC = "decode attn µs/layer + HBM GB/s at 32K ctx; prefill attn tokens/s at 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_decode32k_prefill8k.txt")
 CSRC = os.path.join(ROOT, "long_context_amd", "csrc")
-# library timing name -> the source file that holds its kernel
+# library timing name -> the source files that hold its kernel
 KERNEL_SOURCE = {
-    "decode_attn_dense": "decode.hip", "decode_attn_gather": "decode.hip",
-    "decode_combine": "decode.hip", "topk_decode": "topk.hip", "topk_prefill": "topk.hip",
-    "prefill_dense": "prefill.hip", "prefill_pool": "prefill.hip", "prefill_gather": "prefill.hip",
+    "decode_attn_dense": ("decode.hip",), "decode_attn_gather": ("decode.hip",),
+    "decode_combine": ("decode.hip",), "topk_decode": ("topk.hip",), "topk_prefill": ("topk.hip",),
+    "prefill_dense": ("prefill.hip", "lds_stage.hpp"), "prefill_pool": ("prefill.hip",),
+    "prefill_gather": ("prefill_gather.hip", "prefill.hip", "lds_stage.hpp"),
 }
 
 
@@ -50,7 +51,7 @@ def kernel_source_digest(name):
     device headers and the build flags: a change to any of them makes stored
     counter readings stale."""
     h = hashlib.sha256()
-    for path in (os.path.join(CSRC, KERNEL_SOURCE[name]), os.path.join(CSRC, "device_common.hpp"),
+    for path in (*[os.path.join(CSRC, f) for f in KERNEL_SOURCE[name]], os.path.join(CSRC, "device_common.hpp"),
                  os.path.join(CSRC, "kernels.hpp"), os.path.join(ROOT, "long_context_amd", "build.py")):
         with open(path, "rb") as f:
             h.update(f.read())
