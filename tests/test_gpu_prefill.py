@@ -107,6 +107,37 @@ def test_prefill_reuse_k_eq_n_is_dense(lib, orc):
     check_close(host64(out).reshape(-1, w.d), dense_o, BF16, "k=N reuse vs dense")
 
 
+@pytest.mark.parametrize("tile,d,group", [(128, 128, 4), (64, 64, 2), (128, 64, 1), (64, 128, 1)])
+def test_prefill_reuse_unsorted_padded_lists(lib, orc, tile, d, group):
+    """Reuse lists in any order, with duplicate keys and -1 padding anywhere
+    among a tile's first min(k, prefix) positions, and one tile all padding
+    (its rows give zeros): the kernel must mask per key wherever a key above a
+    row or a padding entry sits, not only in a list's last chunk."""
+    w = _small(f"lists_t{tile}_d{d}_g{group}", wid=964 + tile + d + group, hq=2 * group, hkv=2, d=d,
+               n=1000, k=200, tile=tile)
+    log(f"[prefill] case=unsorted_padded_lists T={tile} d={d} G={group} N={w.n} k={w.k}")
+    (q, k, v), _ = synth.make_stack(w, device="cpu")
+    tiles = _tiles(w)
+    rng = np.random.default_rng(17 + tile + d + group)
+    idx = np.full((w.batch, w.hkv, tiles, w.k), -1, np.int32)
+    for kv in range(w.hkv):
+        for t in range(tiles):
+            prefix = min((t + 1) * tile, w.n)
+            kt = min(w.k, prefix)
+            keys = rng.integers(0, prefix, size=kt).astype(np.int32)  # unsorted, duplicates allowed
+            keys[rng.random(kt) < 0.15] = -1
+            idx[0, kv, t, :kt] = keys
+    empty_t = tiles // 2
+    idx[0, 1, empty_t, :] = -1
+    out = K.reuse_prefill(q.to(DEV), k.to(DEV), v.to(DEV), torch.from_numpy(idx).to(DEV), tile)
+    torch.cuda.synchronize()
+    ref = orc.reuse_prefill(to_oracle(q), to_oracle(k), to_oracle(v), idx, tile)
+    got = host64(out)
+    check_close(got.reshape(-1, d), ref, BF16, f"unsorted padded lists T={tile} d={d}")
+    rows = slice(empty_t * tile, min((empty_t + 1) * tile, w.n))
+    assert np.all(got[0, group:2 * group, rows] == 0.0), "an all-padding list gives zeros"
+
+
 def test_prefill_deterministic(lib):
     w = _small("det", wid=961)
     log("[prefill] case=determinism")
