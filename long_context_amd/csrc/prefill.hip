@@ -68,9 +68,18 @@ constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (log2 units)
 #define KASCADE_REUSE_STAGE 1
 #endif
 
+// d = 64 dense pass: four wavefronts per SIMD (at most 128 VGPRs). Its step is
+// bound by vector work, so the extra wavefronts pay; the next step's K
+// operands are then read after the P.V (kLateK), where the other wavefronts
+// hide their latency, so that the softmax fits in the register budget.
+template <int D, bool GATHER>
+constexpr int attn_waves_per_simd() { return D == 64 && !GATHER ? 4 : 1; }
+
 template <int D, bool GATHER, bool WITH_O, int NH, int KC, int TR, int NB>
-__global__ __launch_bounds__(64 * (TR / kRowsPerWave) * NH) void prefill_attn(PrefillArgs a) {
+__global__ __launch_bounds__(64 * (TR / kRowsPerWave) * NH)
+    __attribute__((amdgpu_waves_per_eu(attn_waves_per_simd<D, GATHER>()))) void prefill_attn(PrefillArgs a) {
   constexpr bool DMA = !GATHER;
+  constexpr bool kLateK = attn_waves_per_simd<D, GATHER>() > 1;
   constexpr int kKeyChunk = KC;
   constexpr int kKeyWaves = KC / 64;  // wavefronts that hold the chunk's list entries (gather)
   constexpr int C = D / 16;           // 16-element contraction chunks of S^T
@@ -290,7 +299,9 @@ __global__ __launch_bounds__(64 * (TR / kRowsPerWave) * NH) void prefill_attn(Pr
     f32x16 s = zero_f32x16();
 #pragma unroll
     for (int cc = 0; cc < C; ++cc) s = mfma32x32x16(kf[cc], bq[cc], s);
-    if (sub + 1 < KC / 32) read_k(buf, sub + 1, kf);  // next step's operands, during this softmax
+    // Next step's K operands: during this softmax, or (kLateK) after this
+    // step's P.V, which keeps them out of the softmax's live registers.
+    if (!kLateK && sub + 1 < KC / 32) read_k(buf, sub + 1, kf);
     if (masked) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -341,6 +352,7 @@ float lsum = 0.f;
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) acc[db] = mfma32x32x16(vf[db][s2], pb[s2], acc[db]);
     }
+    if (kLateK && sub + 1 < KC / 32) read_k(buf, sub + 1, kf);
   };
   auto chunk_step = [&](int buf, int c, bool masked) __attribute__((always_inline)) {
     bf16x8 kf[C];
