@@ -291,9 +291,14 @@ __global__ __launch_bounds__(64 * WAVES) void prefill_reuse_ring(PrefillArgs a) 
       const float mnew = fmaxf(m, cmax);
       alpha = fast_exp2(m - mnew);
       m = mnew;
+      // The accumulators are scaled here rather than after the probabilities:
+      // a second branch on the same condition makes the register allocator
+      // give them two homes and copy them between the two every step.
+#pragma unroll
+      for (int i = 0; i < DB; ++i) acc[i] *= alpha;
     }
     const float neg_m = -m;
-float lsum = 0.f;
+    float lsum = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       s[i] = fast_exp2(fmaf(s[i], sl2, neg_m));
@@ -306,10 +311,6 @@ float lsum = 0.f;
       const f32x4 p0 = {s[8 * s2 + 0], s[8 * s2 + 1], s[8 * s2 + 2], s[8 * s2 + 3]};
       const f32x4 p1 = {s[8 * s2 + 4], s[8 * s2 + 5], s[8 * s2 + 6], s[8 * s2 + 7]};
       pb[s2] = pack_bf16x8(p0, p1);
-    }
-    if (rescale) {
-#pragma unroll
-      for (int i = 0; i < DB; ++i) acc[i] *= alpha;
     }
 #pragma unroll
     for (int db = 0; db < DB; ++db)
