@@ -258,12 +258,22 @@ __global__ __launch_bounds__(64 * WAVES) void prefill_reuse_ring(PrefillArgs a) 
 #pragma unroll
   for (int i = 0; i < DB; ++i) acc[i] = zero_f32x16();
   float m = kNegBig, l = 0.f;
-  bf16x8 kf[C], vf[DB][2];
+  bf16x8 kf[C], vf[DB][2], pb[2];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) vf[i][0] = vf[i][1] = zero_bf16x8();
+  pb[0] = pb[1] = zero_bf16x8();
+  auto pv = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) acc[db] = mfma32x32x16(vf[db][s2], pb[s2], acc[db]);
+  };
 
   bool masked = advance(0);  // chunk 0
   read_k(0, 0, kf);
   for (int j = 0; j < nsteps; ++j) {
     const int c = j / SPC, sub = j % SPC, buf = c & (NB - 1);
+    pv();  // step j - 1 (nothing at j = 0)
     read_v(buf, sub, vf);
     f32x16 s = zero_f32x16();
 #pragma unroll
@@ -305,18 +315,14 @@ __global__ __launch_bounds__(64 * WAVES) void prefill_reuse_ring(PrefillArgs a) 
       lsum += s[i];
     }
     l = l * alpha + lsum;
-    bf16x8 pb[2];
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       const f32x4 p0 = {s[8 * s2 + 0], s[8 * s2 + 1], s[8 * s2 + 2], s[8 * s2 + 3]};
       const f32x4 p1 = {s[8 * s2 + 4], s[8 * s2 + 5], s[8 * s2 + 6], s[8 * s2 + 7]};
       pb[s2] = pack_bf16x8(p0, p1);
     }
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) acc[db] = mfma32x32x16(vf[db][s2], pb[s2], acc[db]);
   }
+  pv();  // the last step
 
   // ---- output: normalised rows through the stage, out in 1-KB pieces ------------
   float lo_, hi_;
