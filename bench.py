@@ -41,7 +41,7 @@ CSRC = os.path.join(ROOT, "long_context_amd", "csrc")
 KERNEL_SOURCE = {
     "decode_attn_dense": ("decode.hip",), "decode_attn_gather": ("decode.hip",),
     "decode_combine": ("decode.hip",), "topk_decode": ("topk.hip",), "topk_prefill": ("topk.hip",),
-    "prefill_dense": ("prefill.hip", "lds_stage.hpp"), "prefill_pool": ("prefill.hip",),
+    "prefill_dense": ("prefill.hip", "lds_stage.hpp"), "prefill_pool": ("prefill.hip", "lds_stage.hpp"),
     "prefill_gather": ("prefill_gather.hip", "prefill.hip", "lds_stage.hpp"),
 }
 

@@ -20,8 +20,9 @@
 // i.e. the post-softmax probabilities summed over the tile (the sum ranks
 // keys as the mean does). The row log-sum-exp must be final before any term
 // is added, so the scores are recomputed rather than stored. Each wave keeps
-// 64 keys of K resident as matrix-core operands and streams the tile's query
-// rows through LDS; column sums are lane-local until one final cross-lane step.
+// 64 keys of K resident as matrix-core operands and streams the group's query
+// rows of the tile through a two-slot LDS ring of 64-row units; column sums
+// are lane-local until one final cross-lane step.
 #include <algorithm>
 
 #include "device_common.hpp"
@@ -34,7 +35,6 @@ namespace {
 
 constexpr int kRowsPerWave = 32;   // query rows per wavefront in prefill_attn
 constexpr int kTile = 128;         // dense-pass work tile: four wavefronts of 32 rows
-constexpr int kLdsPad = 16;        // bf16 elements of padding per LDS row
 constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (log2 units)
 
 // KC keys are staged per pipeline step (64 or 128).
@@ -532,24 +532,39 @@ __host__ __device__ inline int pool_items_before(int t, int tile) {
   return p * q * (q + 1) / 2 + r * (q + 1);
 }
 
-// TP query rows per tile (the selection tile: 64 or 128).
-template <int D, int TP>
-__global__ __launch_bounds__(64 * kPoolWaves) void prefill_pool(PrefillArgs a, int items, int per_xcd) {
-  constexpr int C = D / 32;
-  constexpr int LD = D + kLdsPad;
-  constexpr int THREADS = 64 * kPoolWaves;
-  constexpr int VPR = D / 8;
-  constexpr int LPT = TP * VPR / THREADS;
-  constexpr int kPoolBlocks = TP / 16;  // 16-row blocks per staged head
-  static_assert(LPT >= 1 && TP * VPR % THREADS == 0, "tile rows must split evenly");
-  __shared__ __attribute__((aligned(16))) __bf16 qs[2][TP * LD];
-  __shared__ __attribute__((aligned(16))) float ls[2][TP];
+// The pooled pass is built for occupancy: the matrix and vector work of one
+// wavefront hides behind the other wavefronts of its SIMD. A workgroup (four
+// wavefronts, 256 keys) walks the units of the group's heads for its tile: 64
+// query rows (a head's tile, or half of it), staged by direct global -> LDS
+// loads into a ring of two slots (unpadded rows, 16-byte slots swizzled by
+// swz<D>), unit u + 1 landing while unit u is used. Per 16-row block a
+// wavefront computes its 16 x 64 scores and their exp2/sum work with few
+// operands live, and the LDS footprint stays near 32 KiB at d = 128. A unit
+// whose rows lie wholly before the wavefront's keys costs nothing but its
+// share of the loads.
+constexpr int kPoolUnit = 64;  // query rows per staged unit
 
-  // Workgroups go round-robin to the 8 XCDs; items are dealt so that each XCD
-  // takes a contiguous run (the chunks of a tile share its query rows in L2).
+// Wavefronts per SIMD: three at d = 128, with each block's Q operands read
+// during the previous block's vector work (155 VGPRs); five at d = 64, one
+// block's operands at a time (86 VGPRs). Four at d = 128 without the early
+// reads spilled and measured the same.
+template <int D>
+constexpr int pool_waves_per_simd() { return D == 128 ? 3 : 5; }
+
+template <int D, int TP>
+__global__ __launch_bounds__(64 * kPoolWaves) __attribute__((amdgpu_waves_per_eu(pool_waves_per_simd<D>())))
+void prefill_pool(PrefillArgs a, int items, int per_xcd) {
+  constexpr int C = D / 32;
+  constexpr bool PF = D == 128;  // Q operands one block ahead
+  constexpr int SLOTS = D / 8;                                   // 16-byte slots per row
+  constexpr int DPW = kPoolUnit * D * 2 / (kPoolWaves * 1024);   // 1 KiB direct loads per wave and unit
+  static_assert(DPW >= 1 && kPoolUnit * D * 2 == DPW * kPoolWaves * 1024, "unit must split evenly");
+  static_assert(TP % kPoolUnit == 0, "tile must hold whole units");
+  __shared__ __attribute__((aligned(16))) __bf16 qs[2][kPoolUnit * D];
+  __shared__ __attribute__((aligned(16))) float ls[2][kPoolUnit];
+
   const int item = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
   if (item >= items) return;
-  // items_before(t) ~ t^2 T / 512: start from that estimate, then step.
   int t = max(0, (int)sqrtf(512.0f / TP * (float)item) - 1);
   while (pool_items_before(t + 1, TP) <= item) ++t;
   while (t > 0 && pool_items_before(t, TP) > item) --t;
@@ -561,9 +576,11 @@ __global__ __launch_bounds__(64 * kPoolWaves) void prefill_pool(PrefillArgs a, i
   const int row0 = t * TP;
   const int prefix = min(row0 + TP, a.n);
   const float sl2 = a.scale_log2;
+  // Units of the tile that hold rows below N (one or two per head); unit u
+  // is head u / 2 and rows row0 + 64 (u % 2) onward when there are two.
+  const bool two = prefix - row0 > kPoolUnit;
+  const int units = two ? 2 * a.group : a.group;
 
-  // K^T operands of this wave's 64 keys (keys past N read row 0 and are never
-  // written out).
   const u16* kb = a.k + (size_t)(b * a.hkv + kvh) * a.n * D;
   bf16x8 bk[4][C];
 #pragma unroll
@@ -575,45 +592,36 @@ __global__ __launch_bounds__(64 * kPoolWaves) void prefill_pool(PrefillArgs a, i
   }
   float colsum[4] = {0.f, 0.f, 0.f, 0.f};
 
-  // One step stages the tile's rows of one head of the group.
-  bf16x8 qr[LPT];
+  // Direct load i of this wave fills LDS slot position q % SLOTS of unit row
+  // q / SLOTS, q = 64 (DPW wave + i) + lane, with source slot pos ^ swz(row).
   float lr = INFINITY;
-  // Rows are addressed from the tile's first row (a wave-uniform base) with
-  // 32-bit byte offsets below TP * D * 2; rows past N repeat row N - 1.
-  const int last_row = a.n - 1 - row0;
-  auto fetch = [&](int step) __attribute__((always_inline)) {
-    const int h = kvh * a.group + step;
-    const unsigned char* qt =
-        reinterpret_cast<const unsigned char*>(a.q + ((size_t)(b * a.hq + h) * a.n + row0) * D);
+  auto issue = [&](int u) __attribute__((always_inline)) {
+    const int h = kvh * a.group + (two ? u >> 1 : u);
+    const int ur0 = row0 + (two ? kPoolUnit * (u & 1) : 0);
+    const int last = a.n - 1 - ur0;  // >= 0: the unit starts below N
+    const u16* src = a.q + ((size_t)(b * a.hq + h) * a.n + ur0) * D;
+    const unsigned lds = lds_address(&qs[u & 1][0]) + (unsigned)(wave * DPW) * 1024u;
+    // The row log-sum-exp first: nothing between the direct loads and the
+    // unit's compute then waits on the memory counter.
+    if (wave == 0) lr = lane <= last ? a.lse2[(size_t)(b * a.hq + h) * a.n + ur0 + lane] : INFINITY;
 #pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int slot = tid + i * THREADS;
-      const int row = slot / VPR, col = (slot % VPR) * 8;
-      qr[i] = *reinterpret_cast<const bf16x8*>(qt + (unsigned)(min(row, last_row) * D + col) * 2u);
-    }
-    if (tid < TP) {
-      const int row = row0 + tid;
-      // Rows past N get +inf so that every probability they add is 0.
-      lr = row < a.n ? a.lse2[(size_t)(b * a.hq + h) * a.n + row] : INFINITY;
+    for (int i = 0; i < DPW; ++i) {
+      const int r = (64 / SLOTS) * (DPW * wave + i) + lane / SLOTS, pos = lane % SLOTS;
+      const unsigned off = (unsigned)(min(r, last) * D + 8 * (pos ^ swz<D>(r))) * 2u;
+      lds_dma16_at(src, off, lds + 1024u * i);
     }
   };
-  auto stash = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int slot = tid + i * THREADS;
-      const int row = slot / VPR, col = (slot % VPR) * 8;
-      *reinterpret_cast<bf16x8*>(&qs[buf][row * LD + col]) = qr[i];
-    }
-    if (tid < TP) ls[buf][tid] = lr;
+  auto land = [&](int u) __attribute__((always_inline)) {
+    wait_vm(0);
+    if (wave == 0) ls[u & 1][lane] = lr;
   };
   auto read_q = [&](int buf, int rb, bf16x8 (&aq)[C], f32x4& lse) __attribute__((always_inline)) {
+    const int row = 16 * rb + n16;
 #pragma unroll
     for (int c = 0; c < C; ++c)
-      aq[c] = *reinterpret_cast<const bf16x8*>(&qs[buf][(16 * rb + n16) * LD + 32 * c + 8 * qg]);
+      aq[c] = *reinterpret_cast<const bf16x8*>(&qs[buf][row * D + 8 * ((4 * c + qg) ^ swz<D>(row))]);
     lse = *reinterpret_cast<const f32x4*>(&ls[buf][16 * rb + 4 * qg]);
   };
-  // S[16 rows x 64 keys] of one row block: lane holds rows 4qg..4qg+3 of key
-  // column n16 of each 16-key tile.
   auto scores = [&](const bf16x8 (&aq)[C], f32x4 (&s)[4]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -622,48 +630,40 @@ __global__ __launch_bounds__(64 * kPoolWaves) void prefill_pool(PrefillArgs a, i
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) s[kt] = mfma16x16x32(aq[c], bk[kt][c], s[kt]);
   };
-  auto accumulate = [&](const f32x4 (&s)[4], f32x4 lse) __attribute__((always_inline)) {
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) colsum[kt] += fast_exp2(fmaf(s[kt][r], sl2, -lse[r]));
-  };
 
-  fetch(0);
-  stash(0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K operands in place before the loop
+  issue(0);
+  land(0);
   __syncthreads();
-  if (a.group > 1) fetch(1);
-  for (int step = 0; step < a.group; ++step) {
-    const int buf = step & 1;
-    if (wkey0 + kPoolKeysPerWave - 1 <= row0) {
-      // Every key of the wave is visible to every row of the tile. Three-stage
-      // pipeline over the row blocks: LDS reads two blocks ahead, matrix-core
-      // scores one block ahead, exp2 and column sums of the current block.
-      bf16x8 aq[3][C];
-      f32x4 lq[3], sc[2][4];
-      read_q(buf, 0, aq[0], lq[0]);
-      read_q(buf, 1, aq[1], lq[1]);
-      scores(aq[0], sc[0]);
+  for (int u = 0; u < units; ++u) {
+    const int buf = u & 1;
+    if (u + 1 < units) issue(u + 1);
+    const int ur0 = row0 + (two ? kPoolUnit * (u & 1) : 0);
+    if (wkey0 + kPoolKeysPerWave - 1 <= ur0) {
+      // Every key of the wave is visible to every row of the unit.
+      bf16x8 aq[PF ? 2 : 1][C];
+      f32x4 lq[PF ? 2 : 1];
+      if (PF) read_q(buf, 0, aq[0], lq[0]);
 #pragma unroll
-      for (int rb = 0; rb < kPoolBlocks; ++rb) {
-        if (rb + 2 < kPoolBlocks) read_q(buf, rb + 2, aq[(rb + 2) % 3], lq[(rb + 2) % 3]);
-        if (rb + 1 < kPoolBlocks) scores(aq[(rb + 1) % 3], sc[(rb + 1) & 1]);
-        accumulate(sc[rb & 1], lq[rb % 3]);
-        // Issue order: the block's LDS reads, then each matrix-core step
-        // followed by three vector-ALU instructions of the current block.
-        __builtin_amdgcn_sched_group_barrier(0x100, C + 1, 0);
+      for (int rb = 0; rb < kPoolUnit / 16; ++rb) {
+        const int cur = PF ? rb & 1 : 0;
+        f32x4 s[4];
+        if (!PF) read_q(buf, rb, aq[0], lq[0]);
+        scores(aq[cur], s);
+        // With PF the next block's operands are read during this block's
+        // vector work.
+        if (PF && rb + 1 < kPoolUnit / 16) read_q(buf, rb + 1, aq[cur ^ 1], lq[cur ^ 1]);
 #pragma unroll
-        for (int i = 0; i < 4 * C; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-        }
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) colsum[kt] += fast_exp2(fmaf(s[kt][r], sl2, -lq[cur][r]));
+        // Blocks stay in order, so that no more operands are live at once.
+        __builtin_amdgcn_sched_barrier(0);
       }
-    } else if (wkey0 < prefix) {
+    } else if (wkey0 < prefix && wkey0 <= ur0 + kPoolUnit - 1) {
       // Diagonal: key j counts for row i only when j <= i.
 #pragma unroll 1
-      for (int rb = 0; rb < kPoolBlocks; ++rb) {
-        const int rr0 = row0 + 16 * rb;
+      for (int rb = 0; rb < kPoolUnit / 16; ++rb) {
+        const int rr0 = ur0 + 16 * rb;
         if (rr0 + 15 < wkey0 || rr0 >= prefix) continue;  // no key of the wave is visible
         bf16x8 aq[C];
         f32x4 lse, s[4];
@@ -680,9 +680,8 @@ __global__ __launch_bounds__(64 * kPoolWaves) void prefill_pool(PrefillArgs a, i
         }
       }
     }
-    if (step + 1 < a.group) stash(buf ^ 1);
+    if (u + 1 < units) land(u + 1);
     __syncthreads();
-    if (step + 2 < a.group) fetch(step + 2);
   }
 
   const size_t ragged = prefill_ragged_len(a.n, TP);
