@@ -544,18 +544,14 @@ __host__ __device__ inline int pool_items_before(int t, int tile) {
 // share of the loads.
 constexpr int kPoolUnit = 64;  // query rows per staged unit
 
-// Wavefronts per SIMD: three at d = 128, with each block's Q operands read
-// during the previous block's vector work (155 VGPRs); five at d = 64, one
-// block's operands at a time (86 VGPRs). Four at d = 128 without the early
-// reads spilled and measured the same.
+// Wavefronts per SIMD: four at d = 128 (128 VGPRs), five at d = 64 (85).
 template <int D>
-constexpr int pool_waves_per_simd() { return D == 128 ? 3 : 5; }
+constexpr int pool_waves_per_simd() { return D == 128 ? 4 : 5; }
 
 template <int D, int TP>
 __global__ __launch_bounds__(64 * kPoolWaves) __attribute__((amdgpu_waves_per_eu(pool_waves_per_simd<D>())))
 void prefill_pool(PrefillArgs a, int items, int per_xcd) {
   constexpr int C = D / 32;
-  constexpr bool PF = D == 128;  // Q operands one block ahead
   constexpr int SLOTS = D / 8;                                   // 16-byte slots per row
   constexpr int DPW = kPoolUnit * D * 2 / (kPoolWaves * 1024);   // 1 KiB direct loads per wave and unit
   static_assert(DPW >= 1 && kPoolUnit * D * 2 == DPW * kPoolWaves * 1024, "unit must split evenly");
@@ -594,16 +590,19 @@ void prefill_pool(PrefillArgs a, int items, int per_xcd) {
 
   // Direct load i of this wave fills LDS slot position q % SLOTS of unit row
   // q / SLOTS, q = 64 (DPW wave + i) + lane, with source slot pos ^ swz(row).
-  float lr = INFINITY;
+  int last_u = 0;  // last row of the unit issued last, from its first row
   auto issue = [&](int u) __attribute__((always_inline)) {
     const int h = kvh * a.group + (two ? u >> 1 : u);
     const int ur0 = row0 + (two ? kPoolUnit * (u & 1) : 0);
     const int last = a.n - 1 - ur0;  // >= 0: the unit starts below N
     const u16* src = a.q + ((size_t)(b * a.hq + h) * a.n + ur0) * D;
     const unsigned lds = lds_address(&qs[u & 1][0]) + (unsigned)(wave * DPW) * 1024u;
-    // The row log-sum-exp first: nothing between the direct loads and the
-    // unit's compute then waits on the memory counter.
-    if (wave == 0) lr = lane <= last ? a.lse2[(size_t)(b * a.hq + h) * a.n + ur0 + lane] : INFINITY;
+    // The rows' log2-sum-exp straight into LDS as well (rows past N read row
+    // N - 1 and are set to +inf once the load has landed, so that they add 0).
+    if (wave == 0)
+      lds_dma4_at(a.lse2 + (size_t)(b * a.hq + h) * a.n + ur0, (unsigned)min(lane, last) * 4u,
+                  lds_address(&ls[u & 1][0]));
+    last_u = last;
 #pragma unroll
     for (int i = 0; i < DPW; ++i) {
       const int r = (64 / SLOTS) * (DPW * wave + i) + lane / SLOTS, pos = lane % SLOTS;
@@ -613,7 +612,10 @@ void prefill_pool(PrefillArgs a, int items, int per_xcd) {
   };
   auto land = [&](int u) __attribute__((always_inline)) {
     wait_vm(0);
-    if (wave == 0) ls[u & 1][lane] = lr;
+    if (wave == 0 && last_u < kPoolUnit - 1) {
+      const int ml = __lane_id();  // not kept live through the loop
+      if (ml > last_u) ls[u & 1][ml] = INFINITY;
+    }
   };
   auto read_q = [&](int buf, int rb, bf16x8 (&aq)[C], f32x4& lse) __attribute__((always_inline)) {
     const int row = 16 * rb + n16;
@@ -640,23 +642,18 @@ void prefill_pool(PrefillArgs a, int items, int per_xcd) {
     const int ur0 = row0 + (two ? kPoolUnit * (u & 1) : 0);
     if (wkey0 + kPoolKeysPerWave - 1 <= ur0) {
       // Every key of the wave is visible to every row of the unit.
-      bf16x8 aq[PF ? 2 : 1][C];
-      f32x4 lq[PF ? 2 : 1];
-      if (PF) read_q(buf, 0, aq[0], lq[0]);
 #pragma unroll
       for (int rb = 0; rb < kPoolUnit / 16; ++rb) {
-        const int cur = PF ? rb & 1 : 0;
-        f32x4 s[4];
-        if (!PF) read_q(buf, rb, aq[0], lq[0]);
-        scores(aq[cur], s);
-        // With PF the next block's operands are read during this block's
-        // vector work.
-        if (PF && rb + 1 < kPoolUnit / 16) read_q(buf, rb + 1, aq[cur ^ 1], lq[cur ^ 1]);
+        bf16x8 aq[C];
+        f32x4 lse, s[4];
+        read_q(buf, rb, aq, lse);
+        scores(aq, s);
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) colsum[kt] += fast_exp2(fmaf(s[kt][r], sl2, -lq[cur][r]));
-        // Blocks stay in order, so that no more operands are live at once.
+          for (int r = 0; r < 4; ++r) colsum[kt] += fast_exp2(fmaf(s[kt][r], sl2, -lse[r]));
+        // One block's operands live at a time: the other wavefronts of the
+        // SIMD fill the gaps.
         __builtin_amdgcn_sched_barrier(0);
       }
     } else if (wkey0 < prefix && wkey0 <= ur0 + kPoolUnit - 1) {

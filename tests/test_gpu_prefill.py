@@ -28,6 +28,8 @@ def _small(name, **kw):
 CASES = {
     "d128_ragged": _small("d128_ragged"),
     "d64_g8": _small("d64_g8", wid=951, hq=16, hkv=2, d=64, n=700, k=160),
+    # d = 64 with a last tile that ends inside its second 64-row half
+    "d64_half_tile": _small("d64_half_tile", wid=964, hq=8, hkv=2, d=64, n=1000, k=256),
     "batch2_g1": _small("batch2_g1", wid=952, batch=2, hq=2, hkv=2, n=520, k=200),
     "k_ge_n": _small("k_ge_n", wid=953, n=300, k=512),
     "k_below_tile": _small("k_below_tile", wid=954, n=450, k=40),
