@@ -30,6 +30,10 @@ CASES = {
     "d64_g8": _small("d64_g8", wid=951, hq=16, hkv=2, d=64, n=700, k=160),
     # d = 64 with a last tile that ends inside its second 64-row half
     "d64_half_tile": _small("d64_half_tile", wid=964, hq=8, hkv=2, d=64, n=1000, k=256),
+    # last tile of exactly 64 rows (one staged unit), and of 65 (a second unit
+    # holding a single row)
+    "d128_tile_64_rows": _small("d128_tile_64_rows", wid=965, n=576, k=200),
+    "d64_tile_65_rows": _small("d64_tile_65_rows", wid=966, hq=8, hkv=2, d=64, n=577, k=200),
     "batch2_g1": _small("batch2_g1", wid=952, batch=2, hq=2, hkv=2, n=520, k=200),
     "k_ge_n": _small("k_ge_n", wid=953, n=300, k=512),
     "k_below_tile": _small("k_below_tile", wid=954, n=450, k=40),
