@@ -309,6 +309,58 @@ def profile_pass(kind, reps, workloads=("decode_llama8b_32k", "prefill_8k")):
     print(json.dumps({"profile_pass": "kernels", "reps": reps, "workloads": list(workloads)}), flush=True)
 
 
+def probe_mix(iters=4096, reps=3):
+    """Vector/matrix overlap of the prefill kernels' inner mixes on registers
+    and LDS only (long_context_amd/csrc/probe/mix_probe.hip): the pooled pass's
+    16-row block at one to six wavefronts per SIMD, and the attention step with
+    operands one step ahead or just in time, with no synchronisation, a
+    workgroup barrier per step, or an LDS-counter wait that allows one step of
+    slack. The grid puts the given number of wavefronts on each of the 1024
+    SIMDs. Times are HIP events around each launch (median of `reps`, after a
+    warm-up that brings the clock up); under rocprofv3 --kernel-trace the
+    dispatches give the kernel durations. One JSON line per configuration."""
+    import ctypes
+    from long_context_amd import build as B
+    lib = ctypes.CDLL(B.PROBE_LIBRARY)
+    lib.kascade_probe_mix.argtypes = [ctypes.c_int] * 5 + [ctypes.c_void_p] * 2
+    lib.kascade_probe_mix.restype = ctypes.c_int
+    out = torch.empty(256 * 256 * 6, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    mfma_flops = {("pool", 128): 16 * 16 * 16 * 32 * 2, ("pool", 64): 8 * 16 * 16 * 32 * 2,
+                  ("attn", 128): 16 * 32 * 32 * 16 * 2, ("attn", 64): 8 * 32 * 32 * 16 * 2}
+    modes = {0: "operands one step ahead", 1: "ahead + barrier per step", 2: "just in time + barrier per step",
+             3: "ahead + LDS-counter wait, one step of slack"}
+    configs = [("pool", 0, d, wps) for d in (128, 64) for wps in range(1, 7)]
+    configs += [("attn", m, 128, wps) for m, wps in ((0, 2), (1, 2), (1, 3), (2, 2), (2, 3), (3, 2))]
+    configs += [("attn", m, 64, 3) for m in (0, 1, 2, 3)]
+
+    def launch(kind, mode, d, wps):
+        rc = lib.kascade_probe_mix(0 if kind == "pool" else 1, mode, d, wps, iters, out.data_ptr(), stream)
+        assert rc == 0, (kind, mode, d, wps, rc)
+
+    for _ in range(20):  # clock warm-up
+        launch("pool", 0, 128, 4)
+    torch.cuda.synchronize()
+    for kind, mode, d, wps in configs:
+        launch(kind, mode, d, wps)
+        times = []
+        for _ in range(reps):
+            a, b = _event(), _event()
+            a.record()
+            launch(kind, mode, d, wps)
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b) * 1e-3)
+        t = float(np.median(times))
+        waves = 256 * wps * 4
+        frac = waves * iters * mfma_flops[(kind, d)] / t / (PEAK_BF16_TFLOPS * 1e12)
+        row = {"probe": "mix", "kind": kind, "d": d, "waves_per_simd": wps, "ms": round(t * 1e3, 3),
+               "of_bf16_peak": round(frac, 3)}
+        if kind == "attn":
+            row["mode"] = modes[mode]
+        print(json.dumps(row), flush=True)
+
+
 def probe_gather(reps=5, workload="decode_llama8b_32k"):
     """Cold-cache memory ceiling of the decode reuse layer's access pattern.
 
@@ -535,8 +587,9 @@ def main():
                     help="run a short pass for rocprofv3 counters instead of the benchmark")
     ap.add_argument("--profile-workloads", default="decode_llama8b_32k,prefill_8k",
                     help="comma-separated synthetic workloads for --profile-pass kernels")
-    ap.add_argument("--probe", choices=("gather",),
-                    help="cold-cache memory ceiling of the decode reuse gather (load-only probe sweep)")
+    ap.add_argument("--probe", choices=("gather", "mix"),
+                    help="gather: cold-cache memory ceiling of the decode reuse gather (load-only probe "
+                         "sweep); mix: vector/matrix overlap of the prefill kernels' inner mixes")
     ap.add_argument("--probe-workload", default="decode_llama8b_32k")
     ap.add_argument("--sweep", action="store_true",
                     help="accuracy against dense attention over k = N/64 ... N/4 (one JSON line per k)")
@@ -553,6 +606,9 @@ def main():
         return
     if args.probe == "gather":
         probe_gather(workload=args.probe_workload)
+        return
+    if args.probe == "mix":
+        probe_mix()
         return
     if args.sweep:
         for w in sweep_workloads():
