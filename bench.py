@@ -315,7 +315,7 @@ def probe_mix(iters=4096, reps=3):
     16-row block at one to six wavefronts per SIMD, and the attention step with
     operands one step ahead or just in time, with no synchronisation, a
     workgroup barrier per step, or an LDS-counter wait that allows one step of
-    slack. The grid puts the given number of wavefronts on each of the 1024
+    slack, and once with K resident in registers. The grid puts the given number of wavefronts on each of the 1024
     SIMDs. Times are HIP events around each launch (median of `reps`, after a
     warm-up that brings the clock up); under rocprofv3 --kernel-trace the
     dispatches give the kernel durations. One JSON line per configuration."""
@@ -329,10 +329,10 @@ def probe_mix(iters=4096, reps=3):
     mfma_flops = {("pool", 128): 16 * 16 * 16 * 32 * 2, ("pool", 64): 8 * 16 * 16 * 32 * 2,
                   ("attn", 128): 16 * 32 * 32 * 16 * 2, ("attn", 64): 8 * 32 * 32 * 16 * 2}
     modes = {0: "operands one step ahead", 1: "ahead + barrier per step", 2: "just in time + barrier per step",
-             3: "ahead + LDS-counter wait, one step of slack"}
+             3: "ahead + LDS-counter wait, one step of slack", 4: "ahead, K resident (V^T the only LDS reads)"}
     configs = [("pool", 0, d, wps) for d in (128, 64) for wps in range(1, 7)]
-    configs += [("attn", m, 128, wps) for m, wps in ((0, 2), (1, 2), (1, 3), (2, 2), (2, 3), (3, 2))]
-    configs += [("attn", m, 64, 3) for m in (0, 1, 2, 3)]
+    configs += [("attn", m, 128, wps) for m, wps in ((0, 2), (1, 2), (2, 2), (2, 3), (3, 2), (4, 2))]
+    configs += [("attn", m, 64, 3) for m in (0, 1, 2, 3, 4)]
 
     def launch(kind, mode, d, wps):
         rc = lib.kascade_probe_mix(0 if kind == "pool" else 1, mode, d, wps, iters, out.data_ptr(), stream)

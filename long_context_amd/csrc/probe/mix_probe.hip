@@ -16,7 +16,9 @@
 //     mode 2: each MFMA's operands read just before it, barrier per step;
 //     mode 3: as 0, but instead of a barrier each wavefront waits (bounded
 //             spin on an LDS counter) until every wavefront of the workgroup
-//             has finished the step before the previous one.
+//             has finished the step before the previous one;
+//     mode 4: as 0, but K stays in registers (read from LDS once), so that
+//             the step's LDS traffic is the V^T reads alone.
 // Results are folded into `out` so that nothing is optimised away. Used by
 // bench.py --probe mix.
 #include <hip/hip_runtime.h>
@@ -84,11 +86,14 @@ void attn_mix(float* out, int iters, float sl2) {
   const int kswz = col & 15;
   const int vL = lane & 15, vg = lane >> 4;
   const int vrow = 4 * (vg >> 1) + (vL >> 2), vslot = 2 * (vg & 1) + ((vL & 3) >> 1);
+  // The tile never changes, so the compiler would hoist every K read out of
+  // the loop; an offset it cannot see through (always 0) keeps them in.
+  int koff = 0;
   auto kread = [&](int c) -> bf16x8 {
-    return *reinterpret_cast<const bf16x8*>(ks + col * 256 + 16 * ((2 * c + hf) ^ kswz));
+    return *reinterpret_cast<const bf16x8*>(ks + koff + col * 256 + 16 * ((2 * c + hf) ^ kswz));
   };
   auto vread = [&](int db, int s2) -> bf16x8 {
-    const unsigned char* v0 = vs + vrow * 256;
+    const unsigned char* v0 = vs + koff + vrow * 256;
     const int off0 = 16 * ((vslot + 4 * db) ^ (vrow & 15)) + 8 * (vL & 1);
     const int off1 = 16 * ((vslot + 4 * db) ^ ((vrow + 8) & 15)) + 8 * (vL & 1);
     const lds_bf16x4 lo = lds_read_transposed(reinterpret_cast<const __bf16*>(v0 + (16 * s2) * 256 + off0));
@@ -109,6 +114,7 @@ void attn_mix(float* out, int iters, float sl2) {
   }
   pb[0] = pb[1] = q[0];
   for (int it = 0; it < iters; ++it) {
+    asm volatile("" : "+v"(koff));
     if constexpr (MODE == 1 || MODE == 2) __syncthreads();
     if constexpr (MODE == 3) {
       const int target = 4 * (it - 1);
@@ -129,8 +135,10 @@ void attn_mix(float* out, int iters, float sl2) {
         for (int s2 = 0; s2 < 2; ++s2) vf[d][s2] = vread(d, s2);
 #pragma unroll
       for (int c = 0; c < C; ++c) s = mfma32x32x16(kf[c], q[c], s);
+      if constexpr (MODE != 4) {
 #pragma unroll
-      for (int c = 0; c < C; ++c) kf[c] = kread(c);
+        for (int c = 0; c < C; ++c) kf[c] = kread(c);
+      }
     } else {
 #pragma unroll
       for (int c = 0; c < C; ++c) s = mfma32x32x16(kread(c), q[c], s);
@@ -182,19 +190,19 @@ hipError_t launch_attn_mix(int wps, int blocks, float* out, int iters, hipStream
 
 }  // namespace
 
-// kind 0: pooled-pass mix, kind 1: attention step (mode 0..3, see above).
-// d: 64 or 128. waves_per_simd: 1..6 (pool), 1..3 (attention; at most 2 for
-// modes 0 and 3 at d = 128); the grid is
+// kind 0: pooled-pass mix, kind 1: attention step (mode 0..4, see above).
+// d: 64 or 128. waves_per_simd: 1..6 (pool), 1..3 (attention; at most 2 at
+// d = 128 except for mode 2); the grid is
 // 256 * waves_per_simd workgroups of four wavefronts, so that each of the
 // 1024 SIMDs holds that many. out: at least 256 * 256 * waves_per_simd floats.
 // Returns 0, 1 for an invalid argument, 4 for a launch error.
 extern "C" int kascade_probe_mix(int kind, int mode, int d, int waves_per_simd, int iters, float* out,
                                  void* stream) {
   if (!out || iters < 1 || (d != 64 && d != 128) || waves_per_simd < 1 || waves_per_simd > 6) return 1;
-  if (kind == 1 && (mode < 0 || mode > 3 || waves_per_simd > 3)) return 1;
-  // At d = 128, modes 0 and 3 hold a step of operands ahead (about 190 VGPRs):
-  // at most two wavefronts per SIMD.
-  if (kind == 1 && d == 128 && (mode == 0 || mode == 3) && waves_per_simd > 2) return 1;
+  if (kind == 1 && (mode < 0 || mode > 4 || waves_per_simd > 3)) return 1;
+  // At d = 128 the modes that hold a step of operands ahead need 170-200
+  // VGPRs: at most two wavefronts per SIMD.
+  if (kind == 1 && d == 128 && mode != 2 && waves_per_simd > 2) return 1;
   const int blocks = 256 * waves_per_simd;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
@@ -206,7 +214,8 @@ extern "C" int kascade_probe_mix(int kind, int mode, int d, int waves_per_simd, 
 #define MIX(M)                                                                                 \
   e = d == 128 ? launch_attn_mix<M, 128>(waves_per_simd, blocks, out, iters, s)              \
                : launch_attn_mix<M, 64>(waves_per_simd, blocks, out, iters, s)
-    if (mode == 0) MIX(0); else if (mode == 1) MIX(1); else if (mode == 2) MIX(2); else MIX(3);
+    if (mode == 0) MIX(0); else if (mode == 1) MIX(1); else if (mode == 2) MIX(2); else if (mode == 3) MIX(3);
+    else MIX(4);
 #undef MIX
   } else {
     return 1;
