@@ -23,9 +23,10 @@
 //
 // Decode fuses the pooling: the segment of KV head kv is produced here from
 // the group's scaled logits and row log-sum-exps, sum over heads of
-// exp2(logit - lse2), straight into registers. Heads are summed in order; for
-// each head a thread has eight 16-byte loads in flight, which keeps enough
-// bytes moving per compute unit to stream the logits.
+// exp2(logit - lse2), straight into registers. Heads are summed in order; a
+// thread issues eight 16-byte loads per head and requests the next head's
+// before summing the current one, which keeps enough bytes moving per
+// compute unit to stream the logits.
 //
 // One set shared by all heads (the non-head-aware ablation) pools first, in a
 // separate pass: decode sums exp2(logit - lse2) over all Hq heads per key;
@@ -322,15 +323,18 @@ __global__ __launch_bounds__(kDecodeThreads) void topk_decode_kernel(const float
   float p[kRegs];
 #pragma unroll
   for (int i = 0; i < kRegs; ++i) p[i] = 0.f;
-  for (int g = 0; g < group; ++g) {
+  // Two heads' rows in flight: head g + 1 is requested before head g is
+  // summed, so each head's load latency hides behind the previous head.
+  auto load_head = [&](int g, float4 (&x)[kRegs / 4]) __attribute__((always_inline)) {
     const float* row = lg + (size_t)g * ld + base;
-    const float m = l2[g];
-    float4 x[kRegs / 4];
 #pragma unroll
     for (int q = 0; q < kRegs / 4; ++q) {
       const int j4 = key_of<NT>(4 * q, tid);
       x[q] = j4 < n_sub ? *reinterpret_cast<const float4*>(row + j4) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+  };
+  auto add_head = [&](int g, const float4 (&x)[kRegs / 4]) __attribute__((always_inline)) {
+    const float m = l2[g];
 #pragma unroll
     for (int q = 0; q < kRegs / 4; ++q) {
       p[4 * q + 0] += fast_exp2(x[q].x - m);
@@ -338,6 +342,15 @@ __global__ __launch_bounds__(kDecodeThreads) void topk_decode_kernel(const float
       p[4 * q + 2] += fast_exp2(x[q].z - m);
       p[4 * q + 3] += fast_exp2(x[q].w - m);
     }
+  };
+  float4 xa[kRegs / 4], xb[kRegs / 4];
+  load_head(0, xa);
+  for (int g = 0; g < group; g += 2) {
+    if (g + 1 < group) load_head(g + 1, xb);
+    add_head(g, xa);
+    if (g + 1 >= group) break;
+    if (g + 2 < group) load_head(g + 2, xa);
+    add_head(g + 1, xb);
   }
   unsigned u[kRegs];
 #pragma unroll
