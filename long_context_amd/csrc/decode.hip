@@ -6,14 +6,16 @@
 // top-k, optionally the dense output); reuse layers run the gather mode over
 // the saved index list (Kascade, euno.news summary, "Methodology" steps 2-3).
 //
-// Work split: each wavefront owns `keys_per_split` consecutive list entries of
-// one (b, KV head) and leaves an unnormalised partial (running max, sum,
-// output) that a small combine kernel merges (split-K decoding).
+// Work split: each wavefront owns a share of one (b, KV head)'s keys and
+// leaves an unnormalised partial (running max, sum, output) that a small
+// combine kernel merges (split-K decoding); the bf16 reuse gather merges them
+// at the end of the same kernel instead (merge_group).
 //
 // bf16 path (matrix cores). For a chunk of 32 keys:
 //   S^T[key, head] = K_chunk[32 x d] . Q_group^T[d x 16]   (heads padded to 16)
 // K rows are loaded straight from HBM as the A operand (16 bytes per lane,
-// four lanes per 64-byte segment of a row), so no LDS is needed. The output
+// four lanes per 64-byte segment of a row), so the operands need no LDS (the
+// anchor's LDS holds only its score buffers). The output
 // O^T[d, head] += V^T[d x 32] . P^T[32 x 16] needs V transposed; each 16x16
 // block of V is transposed exactly by one matrix-core step against a 0/1
 // selector matrix (a bf16 value times 1.0 plus zeros is exact in fp32), which

@@ -3,16 +3,17 @@
 // prefill_attn: flash-style causal attention of one query tile of one head
 // over a key list. Dense mode (anchor pass 1) walks keys 0..prefix_t-1 and
 // writes the per-row log-sum-exp (and, on request, the dense output); gather
-// mode (reuse layer) walks the tile's saved index list, softmax restricted to
-// the saved keys j <= i (Kascade, euno.news summary, "Methodology" steps 3
+// mode (reuse layer; the fallback of prefill_reuse_ring for the shapes that
+// kernel does not take) walks the tile's saved index list, softmax restricted
+// to the saved keys j <= i (Kascade, euno.news summary, "Methodology" steps 3
 // and 6: one index set per query tile, values recomputed with the layer's own
 // tensors).
-//   Per 64-key chunk the workgroup stages K and V rows in LDS (gathered rows
-//   are fetched 16 bytes per lane, 16 lanes per 256-byte row). Each wave owns
-//   32 query rows and computes S^T = K . Q^T on the matrix cores, so the
-//   softmax of a row lives in one lane column (four lanes, two cross-lane
-//   steps per chunk), and O^T += V^T . P^T with P^T taken straight from the
-//   S^T accumulators. V^T operands are read from LDS transposed.
+//   Per chunk the workgroup stages K and V rows in LDS (gathered rows are
+//   fetched 16 bytes per lane, 16 lanes per 256-byte row). Each wave owns 32
+//   query rows and computes S^T = K . Q^T on the matrix cores, so a row's
+//   scores live in two lanes (l and l ^ 32: one cross-lane exchange per
+//   32-key step), and O^T += V^T . P^T with P^T taken straight from the S^T
+//   accumulators. V^T operands are read from LDS transposed.
 //
 // prefill_pool: anchor pass 2. For tile t and key j < prefix_t:
 //   pooled[t, j] = sum over the group's heads and the tile's rows i >= j of
